@@ -1,0 +1,228 @@
+"""Benchmark of the TurboQuant KV-cache hot path on one MI355X.
+
+One step = the whole hot path over one batch of the workload: encode the
+layer's K and V caches (rotation, norm, codebook, packing[, QJL]) and run
+fused decode attention of every query head over the packed cache.
+
+Metric: packed-KV decode-attention GB/s (algorithmic packed bytes read per
+second; `value`), with encode throughput in Mtok/s beside it.  Inputs are
+resident in HBM before timing.  The packed cache and the encode inputs are
+rotated over distinct copies (>= 1 GiB each) so the 256 MB Infinity Cache
+cannot serve a step from the previous one: step i encodes into copy i and
+decodes copy i + R/2, written R/2 steps earlier.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def packed_bytes_per_token_head(w, code_bytes_k, code_bytes_v, sign_bytes_k):
+    kb = code_bytes_k + 2 + (sign_bytes_k + 2 if w.k_qjl else 0)
+    return kb + code_bytes_v + 2
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kv_cache_quantization_05_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel, workload):
+    """HBM bytes per launch measured by rocprofv3 counters, if recorded for the
+    current kernel sources (profiles/traffic.json); otherwise None."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except Exception:
+        return None
+    ent = rec.get(f"{workload}:{kernel}")
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The float64 oracle on the host cores, on a bounded slice of the same
+    workload: one batch element, one KV head (its Hq/Hkv query heads) and the
+    first T_s positions, encode + decode.  Scaled per packed byte / token."""
+    import numpy as np
+    import torch
+
+    from kv_cache_quantization_05_amd import workloads as wl
+    from oracle import decode as odec
+    from oracle import encode as oenc
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    G = w.Hq // w.Hkv
+    kc = oenc.Config(seed=w.seed, head_dim=w.d, bits=w.k_bits, qjl=w.k_qjl)
+    vc = oenc.Config(seed=w.seed, head_dim=w.d, bits=w.v_bits)
+    oenc.get_tables(kc)
+    oenc.get_tables(vc)
+    Ts = 512
+    small = wl.scaled(w, B=1, T=min(w.T, 65536))
+    K, V = wl.kv_pair(small, "cpu")
+    q = wl.queries(w, "cpu")[0, :G].double().numpy()
+    while True:
+        k = K[0, 0, :Ts].float().double().numpy()
+        v = V[0, 0, :Ts].float().double().numpy()
+        t0 = time.perf_counter()
+        kp = oenc.encode(k, kc)
+        vp = oenc.encode(v, vc)
+        t1 = time.perf_counter()
+        kpl = {x: kp[x][None, None] for x in ("codes", "norms", "signs", "rnorms") if x in kp}
+        vpl = {x: vp[x][None, None] for x in ("codes", "norms")}
+        odec.attend_decode(q[None], kpl, vpl, kc, vc, [Ts])
+        t2 = time.perf_counter()
+        if t2 - t0 > budget_s / 4 or Ts * 2 > small.T:
+            break
+        Ts *= 2
+    enc_s, dec_s = t1 - t0, t2 - t1
+    bpt = packed_bytes_per_token_head(w, kc.code_bytes, vc.code_bytes, kc.sign_bytes)
+    dec_gbs = Ts * bpt / dec_s / 1e9
+    # a token = one position across all KV heads, K and V: Hkv x (K + V) vectors
+    enc_mtoks = Ts / (enc_s * w.Hkv) / 1e6
+    return {"value": round(dec_gbs, 6), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"batch 0, KV head 0 ({G} query heads), first {Ts} positions; "
+                      f"encode {enc_s:.2f} s, decode {dec_s:.2f} s; float64 numpy",
+            "encode_mtok_s": round(enc_mtoks, 6)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama_t32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--min-rotation-bytes", type=float, default=1.1 * 2**30)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the single-GPU "
+              f"path is the whole scope of this library.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from kv_cache_quantization_05_amd import binding as tq
+    from kv_cache_quantization_05_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    if w.name == "search_1m":
+        raise SystemExit("search_1m is a parity workload; use a decode workload here")
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    kctx = tq.Context(seed=w.seed, head_dim=w.d, bits=w.k_bits, qjl=w.k_qjl)
+    vctx = tq.Context(seed=w.seed, head_dim=w.d, bits=w.v_bits)
+    K, V = wl.kv_pair(w, dev)
+    q = wl.queries(w, dev)
+    lens = torch.full((w.B,), w.T, dtype=torch.int32, device=dev)
+    in_bytes = (K.numel() + V.numel()) * K.element_size()
+    bpt = packed_bytes_per_token_head(w, kctx.code_bytes, vctx.code_bytes, kctx.sign_bytes)
+    packed = w.B * w.Hkv * w.T * bpt
+    R_in = max(1, math.ceil(args.min_rotation_bytes / in_bytes))
+    R_pk = max(2, math.ceil(args.min_rotation_bytes / packed))
+    inputs = [(K, V)] + [(K.clone(), V.clone()) for _ in range(R_in - 1)]
+    caches = [(kctx.new_planes((w.B, w.Hkv, w.T)), vctx.new_planes((w.B, w.Hkv, w.T))) for _ in range(R_pk)]
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.attend_workspace_bytes(kctx, w.B, w.Hq, w.Hkv, w.T), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(R_pk):  # every copy holds a valid encoding before timing
+        tq.encode(kctx, inputs[i % R_in][0], caches[i][0])
+        tq.encode(vctx, inputs[i % R_in][1], caches[i][1])
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        kin, vin = inputs[i % R_in]
+        kp, vp = caches[i % R_pk]
+        if ev:
+            ev[0].record(stream)
+        tq.encode(kctx, kin, kp)
+        tq.encode(vctx, vin, vp)
+        if ev:
+            ev[1].record(stream)
+        kd, vd = caches[(i + R_pk // 2) % R_pk]
+        tq.attend_decode(kctx, vctx, q, kd, vd, lens, t_max=w.T, out=out, workspace=ws)
+        if ev:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    enc_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    dec_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    enc_avg = sum(enc_ms) / len(enc_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    dec_gbs = packed / (dec_avg * 1e-3) / 1e9
+    enc_bytes = in_bytes + packed
+    enc_gbs = enc_bytes / (enc_avg * 1e-3) / 1e9
+    tokens = w.B * w.T
+    enc_mtoks = tokens / (enc_avg * 1e-3) / 1e6
+
+    def roof(kernel, gbs, alg_bytes, ms):
+        return {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(kernel, w.name),
+                "algorithmic_bytes": int(alg_bytes), "avg_ms": round(ms, 5)}
+
+    r_dec = roof("attend_decode", dec_gbs, packed, dec_avg)
+    r_enc = roof("encode", enc_gbs, enc_bytes, enc_avg)
+    line = {
+        "metric": "packed-KV decode-attention GB/s (% of HBM peak) + encode Mtok/s, 1 GPU",
+        "value": round(dec_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "Hkv": w.Hkv, "Hq": w.Hq, "head_dim": w.d,
+                   "k_bits": w.k_bits, "v_bits": w.v_bits, "k_qjl": w.k_qjl, "input": w.in_dtype,
+                   "packed_bytes": int(packed), "rotation_copies": [R_in, R_pk]},
+        "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+        "decode_us": round(dec_avg * 1e3, 2),
+        "decode_us_p10_p90": [round(dec_ms[len(dec_ms) // 10] * 1e3, 2), round(dec_ms[(9 * len(dec_ms)) // 10] * 1e3, 2)],
+        "encode_us": round(enc_avg * 1e3, 2),
+        "encode_mtok_s": round(enc_mtoks, 2),
+        "roofline": r_enc if enc_avg > dec_avg else r_dec,
+        "roofline_decode": r_dec,
+        "roofline_encode": r_enc,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+/*
+ * tq.h -- C ABI of libtq: TurboQuant KV-cache encode and decode attention on
+ * AMD MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [TQ+ guide]    "TurboQuant+ 上游化实战指南：llama.cpp KV Cache 压缩分支的 4 阶段
+ *                   PR 重构路线图"
+ *   [Orión plan]   "Plan de Integración: TurboQuant en Orión"
+ *   [TQ explainer] "Google TurboQuant 深度解析：KV Cache 压缩的技术革命"
+ *
+ * Conventions (taken from the public-API rules in [TQ+ guide] §2.4 and §9):
+ * fixed-width integers, enum values prefixed with the enum name, snake_case
+ * <class>_<action>_<noun> names, no typedef'd structs.
+ *
+ * Memory: every device buffer (inputs, outputs, workspaces) is allocated and
+ * owned by the caller.  A tq_ctx owns only its small device tables.  No entry
+ * point allocates device memory except tq_ctx_create.
+ *
+ * Errors: arguments are validated on the host before anything is enqueued; a
+ * failed check returns a non-zero tq_status and leaves the stream untouched.
+ * tq_last_error() then describes it (thread-local).  A failed kernel launch
+ * returns TQ_ERR_DEVICE.  Faults inside a kernel surface at the caller's next
+ * synchronisation.  NaN/Inf inputs are not checked; their outputs are
+ * undefined.  No C++ exception crosses this interface.
+ *
+ * Streams: `hip_stream` is a hipStream_t (NULL = the default stream).  All
+ * device work is asynchronous on it.  A ctx is immutable after creation, so
+ * calls on several streams or threads may share one.
+ *
+ * Packed layout (the "planes"): vector v of a plane set occupies
+ *   codes  + v * code_bytes   d*b/8 bytes: code i at bits b*i..b*i+b-1 of an
+ *                             LSB-first bit stream (bit k is bit k%8 of byte
+ *                             k/8); a 32-code block is 4*b bytes
+ *   norms  + v                fp16 bits of ||x||_2 (rounded once, RNE)
+ *   signs  + v * sign_bytes   QJL: m sign bits, bit l = bit l%8 of byte l/8
+ *                             ([Orión plan] Fase 3, sign-bit sketch)
+ *   rnorms + v                QJL: fp16 bits of the residual norm gamma
+ * A plane set addresses a 3-D grid of vectors [n0, n1, n2]; vector (i0,i1,i2)
+ * is v = i0*stride[0] + i1*stride[1] + i2*stride[2].  codes rows must be
+ * 4-byte aligned (d*b/8 is a multiple of 4 for d >= 32).
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum tq_status {
+    TQ_STATUS_OK = 0,
+    TQ_STATUS_INVALID_ARG = 1,
+    TQ_STATUS_UNSUPPORTED = 2,
+    TQ_STATUS_DEVICE = 3,
+    TQ_STATUS_NO_MEMORY = 4,
+};
+
+enum tq_dtype {
+    TQ_DTYPE_F32 = 0,
+    TQ_DTYPE_BF16 = 1,
+};
+
+/*
+ * Method configuration ([TQ+ guide] §5.1-§5.2: MSE-only codebook, block size
+ * 32, rotation width decoupled from block size; [Orión plan] Fase 2 settings
+ * block: separate key and value bit widths -> one config per K and per V).
+ *   seed      seeds the rotation signs D1, D2 and the QJL matrix S
+ *             ([TQ+ guide] §3: rotation generated from a seed, same seed ->
+ *             same matrix)
+ *   head_dim  d: 32, 64, 128 or 256
+ *   bits      b: 2, 3 or 4 bits per coordinate
+ *   block     32 (codes per packed block)
+ *   qjl       1 adds the 1-bit QJL residual sketch ([TQ explainer] §2.2)
+ *   qjl_dim   m, rows of S: 0 means m = d; otherwise a multiple of 32, <= 256
+ */
+struct tq_config {
+    uint64_t seed;
+    int32_t head_dim;
+    int32_t bits;
+    int32_t block;
+    int32_t qjl;
+    int32_t qjl_dim;
+};
+
+/* Opaque, immutable context: the config plus its device tables (D1/D2 sign
+ * masks, fp16-exact Lloyd-Max codebook, thresholds, S).  Bound to the device
+ * current at creation. */
+struct tq_ctx;
+
+/* Vector-grid view of caller-owned packed planes (see the layout above).
+ * signs/rnorms are only used when the ctx has qjl = 1. */
+struct tq_planes {
+    uint8_t * codes;
+    uint16_t * norms;
+    uint8_t * signs;
+    uint16_t * rnorms;
+    int64_t stride[3];
+};
+
+/* Validate cfg, build its tables on the host and upload them to the current
+ * device.  *out receives the ctx on success.  Errors: INVALID_ARG (bad cfg or
+ * NULL), NO_MEMORY, DEVICE. */
+int32_t tq_ctx_create(const struct tq_config * cfg, struct tq_ctx ** out);
+
+/* Release a ctx and its device tables (NULL is ignored).  The caller must
+ * ensure no queued work still uses it. */
+void tq_ctx_free(struct tq_ctx * ctx);
+
+/* Host-only (no device needed): write the tables cfg generates.  Any pointer
+ * may be NULL to skip that table.  d1, d2: d entries of +-1.  codebook: 2^b
+ * fp16-exact centroids, ascending.  thresholds: 2^b - 1 midpoints.
+ * s_rowmajor: m*d entries (only when cfg->qjl).  Rotation: R = D1.H.D2/sqrt(d)
+ * with H the Sylvester Hadamard matrix ([TQ+ guide] §4). */
+int32_t tq_tables_export(const struct tq_config * cfg, int8_t * d1, int8_t * d2,
+                         float * codebook, float * thresholds, float * s_rowmajor);
+
+/* Bytes per vector in each plane for cfg (0 on an invalid cfg). */
+int64_t tq_code_bytes(const struct tq_config * cfg);
+int64_t tq_sign_bytes(const struct tq_config * cfg);
+
+/*
+ * Encode a [n0, n1, n2] grid of d-vectors ([TQ+ guide] §4, §5.1-§5.2;
+ * [Orión plan] Fase 3 sketches; [TQ explainer] §2.2):
+ *   n = ||x||_2 (fp64 accumulation, stored fp16 RNE);
+ *   z = sqrt(d) * R x / n;  code_i = #{k : tau_k < z_i};  pack;
+ *   QJL: rho = (z - c[code]) / sqrt(d), gamma = ||rho|| (fp16), sign bits of
+ *   S rho.
+ * x: device pointer, dtype TQ_DTYPE_F32 or TQ_DTYPE_BF16; element (i0,i1,i2,k)
+ * at x[i0*x_stride[0] + i1*x_stride[1] + i2*x_stride[2] + k] (strides in
+ * elements; the d elements of a vector are contiguous and 16-byte aligned).
+ * out: planes to write (caller-owned device memory).  n0*n1*n2 == 0 is a no-op.
+ * Codes of a coordinate within about 1e-6 of a decision threshold may differ
+ * from a float64 evaluation of the same rule.
+ */
+int32_t tq_encode(const struct tq_ctx * ctx, const void * x, int32_t x_dtype,
+                  int64_t n0, int64_t n1, int64_t n2, const int64_t x_stride[3],
+                  struct tq_planes out, void * hip_stream);
+
+/*
+ * Rotated-query scores against packed keys, straight from the codes
+ * ([TQ+ guide] §5.3 pre-rotate-queries: <q, R^T c> = <R q, c>; [TQ explainer]
+ * §3.2 attention logits from 4-bit keys, §2.2.2 full-precision query):
+ *   s[i, j] = scale * N_j * ( <R q_i, c[code_j]> / sqrt(d)
+ *                             + gamma_j sqrt(pi/2)/m <S R q_i, sigma_j> )
+ * (the second term only for a qjl ctx; sigma = +-1 from the sign bits).
+ * q: device fp32 [n_q, d] dense.  Keys: the n_k vectors at plane offsets
+ * j * k.stride[2] (stride[0], stride[1] unused).
+ * top_k == 0: out_scores is device fp32 [n_q, n_k]; out_idx ignored.
+ * top_k in 1..64: out_scores [n_q, top_k] fp32 and out_idx [n_q, top_k] int64,
+ * best first, equal scores ordered by lower index; the full score matrix is
+ * never stored.  workspace: device memory of tq_scores_workspace() bytes.
+ */
+int32_t tq_scores(const struct tq_ctx * k_ctx, const float * q, int64_t n_q, float scale,
+                  struct tq_planes k, int64_t n_k, int32_t top_k,
+                  float * out_scores, int64_t * out_idx,
+                  void * workspace, int64_t workspace_bytes, void * hip_stream);
+
+int64_t tq_scores_workspace(const struct tq_ctx * k_ctx, int64_t n_q, int64_t n_k, int32_t top_k);
+
+/*
+ * Fused decode attention over packed K and V ([TQ explainer] §4.3:
+ * softmax(q K^T * scale) V; [TQ+ guide] §5.3 pre-rotated query, §6.1 output
+ * rotated back to the original domain):
+ *   out[b, h] = sum_{j < seq_lens[b]} p_j v_hat_j,  p = softmax_j(s_j),
+ *   s_j = scale * <q_{b,h}, k_hat_j>  (QJL-corrected when k_ctx has qjl),
+ * with query head h reading KV head h / (Hq / Hkv).
+ * q: device fp32 [B, Hq, d] dense.  k, v: planes over the grid [B, Hkv, Tcap].
+ * seq_lens: device int32 [B]; entries are clamped to [0, t_max]; a zero
+ * length gives a zero output row.  t_max: host upper bound of seq_lens (sizes
+ * the launch).  out: device fp32 [B, Hq, d] dense.  workspace: device memory
+ * of tq_attend_decode_workspace() bytes.  k_ctx and v_ctx must share
+ * head_dim and seed (the output rotation is v_ctx's); v_ctx must not be qjl.
+ */
+int32_t tq_attend_decode(const struct tq_ctx * k_ctx, const struct tq_ctx * v_ctx,
+                         const float * q, struct tq_planes k, struct tq_planes v,
+                         const int32_t * seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                         int64_t t_max, float scale, float * out,
+                         void * workspace, int64_t workspace_bytes, void * hip_stream);
+
+int64_t tq_attend_decode_workspace(const struct tq_ctx * k_ctx, int32_t B, int32_t Hq,
+                                   int32_t Hkv, int64_t t_max);
+
+/* Thread-local description of the last non-OK status ("" if none). */
+const char * tq_last_error(void);
+
+/* Library version string. */
+const char * tq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -1,0 +1,297 @@
+"""ctypes binding of libtq (include/tq.h): argument marshalling only.
+
+Every step of the method runs inside libtq's HIP kernels; this module turns
+torch tensors into pointers, sizes and strides, and raises TQError with the
+library's message on a non-zero status.  It never computes a result itself
+and has no fallback: if libtq.so is missing or cannot be loaded, every call
+raises.
+"""
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtq.so")
+
+TQ_DTYPE_F32 = 0
+TQ_DTYPE_BF16 = 1
+
+EXPORTED = (
+    "tq_ctx_create", "tq_ctx_free", "tq_tables_export", "tq_code_bytes", "tq_sign_bytes",
+    "tq_encode", "tq_scores", "tq_scores_workspace", "tq_attend_decode",
+    "tq_attend_decode_workspace", "tq_last_error", "tq_version",
+)
+
+
+class TQError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"libtq status {status}: {msg}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("seed", ctypes.c_uint64), ("head_dim", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("qjl", ctypes.c_int32), ("qjl_dim", ctypes.c_int32)]
+
+
+class Planes(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("norms", ctypes.c_void_p), ("signs", ctypes.c_void_p),
+                ("rnorms", ctypes.c_void_p), ("stride", ctypes.c_int64 * 3)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libtq.so once; raises if it is absent (there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libtq.so not built ({LIB_PATH}); run kv_cache_quantization_05_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+        cfgp = ctypes.POINTER(Config)
+        L.tq_ctx_create.argtypes = [cfgp, ctypes.POINTER(vp)]
+        L.tq_ctx_create.restype = i32
+        L.tq_ctx_free.argtypes = [vp]
+        L.tq_ctx_free.restype = None
+        L.tq_tables_export.argtypes = [cfgp, vp, vp, vp, vp, vp]
+        L.tq_tables_export.restype = i32
+        L.tq_code_bytes.argtypes = [cfgp]
+        L.tq_code_bytes.restype = i64
+        L.tq_sign_bytes.argtypes = [cfgp]
+        L.tq_sign_bytes.restype = i64
+        L.tq_encode.argtypes = [vp, vp, i32, i64, i64, i64, ctypes.POINTER(i64), Planes, vp]
+        L.tq_encode.restype = i32
+        L.tq_scores.argtypes = [vp, vp, i64, ctypes.c_float, Planes, i64, i32, vp, vp, vp, i64, vp]
+        L.tq_scores.restype = i32
+        L.tq_scores_workspace.argtypes = [vp, i64, i64, i32]
+        L.tq_scores_workspace.restype = i64
+        L.tq_attend_decode.argtypes = [vp, vp, vp, Planes, Planes, vp, i32, i32, i32, i64,
+                                       ctypes.c_float, vp, vp, i64, vp]
+        L.tq_attend_decode.restype = i32
+        L.tq_attend_decode_workspace.argtypes = [vp, i32, i32, i32, i64]
+        L.tq_attend_decode_workspace.restype = i64
+        L.tq_last_error.argtypes = []
+        L.tq_last_error.restype = ctypes.c_char_p
+        L.tq_version.argtypes = []
+        L.tq_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise TQError(status, lib().tq_last_error().decode())
+
+
+def make_config(seed=0, head_dim=128, bits=3, qjl=False, qjl_dim=0, block=32):
+    return Config(seed, head_dim, bits, block, 1 if qjl else 0, qjl_dim)
+
+
+def tables_export(seed=0, head_dim=128, bits=3, qjl=False, qjl_dim=0):
+    """Host-only copy of the tables libtq builds for a config (no GPU needed)."""
+    import numpy as np
+    cfg = make_config(seed, head_dim, bits, qjl, qjl_dim)
+    m = qjl_dim or head_dim
+    d1 = np.zeros(head_dim, np.int8)
+    d2 = np.zeros(head_dim, np.int8)
+    cb = np.zeros(1 << bits, np.float32)
+    th = np.zeros((1 << bits) - 1, np.float32)
+    S = np.zeros((m, head_dim), np.float32) if qjl else None
+    _check(lib().tq_tables_export(ctypes.byref(cfg), d1.ctypes.data, d2.ctypes.data, cb.ctypes.data,
+                                  th.ctypes.data, S.ctypes.data if S is not None else None))
+    return {"d1": d1, "d2": d2, "codebook": cb, "thresholds": th, "S": S}
+
+
+def code_bytes(head_dim, bits):
+    return lib().tq_code_bytes(ctypes.byref(make_config(0, head_dim, bits)))
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+class Context:
+    """A libtq context (rotation, codebook and QJL tables on the current GPU)."""
+
+    def __init__(self, seed=0, head_dim=128, bits=3, qjl=False, qjl_dim=0):
+        self.cfg = make_config(seed, head_dim, bits, qjl, qjl_dim)
+        self.seed, self.head_dim, self.bits, self.qjl = seed, head_dim, bits, bool(qjl)
+        self.m = qjl_dim or head_dim
+        h = ctypes.c_void_p()
+        _check(lib().tq_ctx_create(ctypes.byref(self.cfg), ctypes.byref(h)))
+        self._h = h
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def code_bytes(self):
+        return self.head_dim * self.bits // 8
+
+    @property
+    def sign_bytes(self):
+        return self.m // 8 if self.qjl else 0
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().tq_ctx_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def new_planes(self, shape, device="cuda"):
+        """Caller-owned dense planes for a vector grid `shape` (1 to 3 dims)."""
+        return PackedPlanes.empty(self, tuple(shape), device)
+
+
+@dataclass
+class PackedPlanes:
+    codes: torch.Tensor    # u8 [..., code_bytes]
+    norms: torch.Tensor    # int16 (fp16 bits) [...]
+    signs: torch.Tensor    # u8 [..., sign_bytes] or None
+    rnorms: torch.Tensor   # int16 [...] or None
+
+    @staticmethod
+    def empty(ctx, shape, device):
+        codes = torch.empty(shape + (ctx.code_bytes,), dtype=torch.uint8, device=device)
+        norms = torch.empty(shape, dtype=torch.int16, device=device)
+        signs = rnorms = None
+        if ctx.qjl:
+            signs = torch.empty(shape + (ctx.sign_bytes,), dtype=torch.uint8, device=device)
+            rnorms = torch.empty(shape, dtype=torch.int16, device=device)
+        return PackedPlanes(codes, norms, signs, rnorms)
+
+    @property
+    def grid(self):
+        return tuple(self.norms.shape)
+
+    def c_struct(self):
+        """Planes struct; strides in vectors from the norms tensor (3-D grid, padded in front)."""
+        st = list(self.norms.stride())
+        st = [0] * (3 - len(st)) + st
+        p = Planes()
+        p.codes = self.codes.data_ptr()
+        p.norms = self.norms.data_ptr()
+        p.signs = self.signs.data_ptr() if self.signs is not None else None
+        p.rnorms = self.rnorms.data_ptr() if self.rnorms is not None else None
+        for i in range(3):
+            p.stride[i] = st[i]
+        return p
+
+    def to(self, device):
+        f = lambda t: t.to(device) if t is not None else None  # noqa: E731
+        return PackedPlanes(f(self.codes), f(self.norms), f(self.signs), f(self.rnorms))
+
+    def numpy(self):
+        out = {"codes": self.codes.cpu().numpy(), "norms": self.norms.cpu().numpy().view("uint16")}
+        if self.signs is not None:
+            out["signs"] = self.signs.cpu().numpy()
+            out["rnorms"] = self.rnorms.cpu().numpy().view("uint16")
+        return out
+
+    @staticmethod
+    def from_numpy(d, device="cuda"):
+        import numpy as np
+        t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(device)  # noqa: E731
+        return PackedPlanes(t(d["codes"], np.uint8), t(d["norms"], np.int16),
+                            t(d["signs"], np.uint8) if "signs" in d else None,
+                            t(d["rnorms"], np.int16) if "rnorms" in d else None)
+
+
+def encode(ctx: Context, x: torch.Tensor, planes: PackedPlanes = None, stream=None):
+    """tq_encode over the vector grid x.shape[:-1] (up to 3 dims).
+
+    x: fp32 or bf16 CUDA tensor [..., d] with a contiguous last dim.
+    planes: output planes over the same grid (allocated if None).
+    """
+    grid = tuple(x.shape[:-1])
+    if len(grid) > 3 or x.shape[-1] != ctx.head_dim or x.stride(-1) != 1:
+        raise ValueError("x must be [..., head_dim] with <= 3 leading dims and unit last stride")
+    if x.dtype == torch.float32:
+        dt = TQ_DTYPE_F32
+    elif x.dtype == torch.bfloat16:
+        dt = TQ_DTYPE_BF16
+    else:
+        raise ValueError("x must be float32 or bfloat16")
+    if planes is None:
+        planes = ctx.new_planes(grid, x.device)
+    if tuple(planes.grid) != grid:
+        raise ValueError("planes grid does not match x")
+    n = [1] * (3 - len(grid)) + list(grid)
+    xs = [0] * (3 - len(grid)) + list(x.stride()[:-1])
+    xs_arr = (ctypes.c_int64 * 3)(*xs)
+    _check(lib().tq_encode(ctx.handle, _ptr(x), dt, n[0], n[1], n[2], xs_arr, planes.c_struct(),
+                           _stream_ptr(stream)))
+    return planes
+
+
+def attend_workspace_bytes(k_ctx, B, Hq, Hkv, t_max):
+    return lib().tq_attend_decode_workspace(k_ctx.handle, B, Hq, Hkv, t_max)
+
+
+def attend_decode(k_ctx: Context, v_ctx: Context, q: torch.Tensor, k: PackedPlanes, v: PackedPlanes,
+                  seq_lens: torch.Tensor, t_max=None, scale=None, out=None, workspace=None, stream=None):
+    """tq_attend_decode.  q: fp32 [B, Hq, d]; k, v: planes over [B, Hkv, Tcap];
+    seq_lens: int32 [B] on the GPU; returns fp32 [B, Hq, d]."""
+    B, Hq, d = q.shape
+    Hkv = k.grid[1]
+    if t_max is None:
+        t_max = k.grid[2]
+    if t_max > k.grid[2] or t_max > v.grid[2]:
+        raise ValueError("t_max exceeds the cache capacity of the planes")
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    need = attend_workspace_bytes(k_ctx, B, Hq, Hkv, t_max)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().tq_attend_decode(k_ctx.handle, v_ctx.handle, _ptr(q), k.c_struct(), v.c_struct(),
+                                  _ptr(seq_lens), B, Hq, Hkv, t_max, ctypes.c_float(scale), _ptr(out),
+                                  _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
+    return out
+
+
+def scores_workspace_bytes(k_ctx, n_q, n_k, top_k):
+    return lib().tq_scores_workspace(k_ctx.handle, n_q, n_k, top_k)
+
+
+def scores(k_ctx: Context, q: torch.Tensor, k: PackedPlanes, top_k=0, scale=1.0, out=None,
+           out_idx=None, workspace=None, stream=None):
+    """tq_scores.  q: fp32 [n_q, d]; k: planes over a 1-D grid [n_k].
+
+    top_k == 0 returns the full [n_q, n_k] score matrix; otherwise
+    (scores [n_q, top_k], indices [n_q, top_k]) best first."""
+    n_q = q.shape[0]
+    n_k = k.grid[-1]
+    if top_k == 0:
+        if out is None:
+            out = torch.empty((n_q, n_k), dtype=torch.float32, device=q.device)
+    else:
+        if out is None:
+            out = torch.empty((n_q, top_k), dtype=torch.float32, device=q.device)
+        if out_idx is None:
+            out_idx = torch.empty((n_q, top_k), dtype=torch.int64, device=q.device)
+    need = scores_workspace_bytes(k_ctx, n_q, n_k, top_k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().tq_scores(k_ctx.handle, _ptr(q), n_q, ctypes.c_float(scale), k.c_struct(), n_k, top_k,
+                           _ptr(out), _ptr(out_idx), _ptr(workspace), workspace.numel(),
+                           _stream_ptr(stream)))
+    return out if top_k == 0 else (out, out_idx)

@@ -1,0 +1,81 @@
+// Internal declarations shared by the host code and the kernel translation
+// units of libtq.  Nothing here is part of the public ABI (include/tq.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+constexpr int kMaxDim = 256;
+
+// Small per-config tables passed to kernels by value (kernel arguments).
+// Sign masks: bit i of word i/32 set means the diagonal entry is -1.
+struct dev_tables {
+    uint32_t d1[kMaxDim / 32];
+    uint32_t d2[kMaxDim / 32];
+    float cb[16];        // codebook, ascending; entries >= 2^b unused
+    float th[16];        // 2^b - 1 thresholds; th[2^b - 1 ..] = +inf
+    const float * S;     // device, m x d row-major (QJL only)
+    int32_t d;
+    int32_t bits;
+    int32_t m;
+    int32_t qjl;
+};
+
+// Host-side table generation (tq_tables.cpp); independent of any device.
+int build_tables(const tq_config & cfg, int8_t * d1, int8_t * d2, float * codebook,
+                 float * thresholds, float * s_rowmajor);
+int validate_config(const tq_config & cfg, const char ** why);
+
+// Launchers (kernel translation units).  Return hipError_t of the launch.
+struct encode_args {
+    const void * x;
+    int32_t dtype;
+    int64_t n0, n1, n2;
+    int64_t xs0, xs1, xs2;      // element strides
+    tq_planes out;
+};
+hipError_t launch_encode(const dev_tables & t, const encode_args & a, hipStream_t s);
+
+// Query preparation: qp[i] = [ R q_i (d floats) | S R q_i (m floats, qjl) ].
+hipError_t launch_query_prep(const dev_tables & t, const float * q, int64_t n, float * qp,
+                             int64_t qp_stride, hipStream_t s);
+
+struct attend_args {
+    const float * qp;           // prepared queries [B*Hq, qp_stride]
+    int64_t qp_stride;
+    tq_planes k, v;
+    const int32_t * seq_lens;
+    int32_t B, Hq, Hkv;
+    int64_t t_max;
+    int32_t chunk;              // tokens per split-K chunk
+    int32_t n_chunks;
+    float scale;
+    float * partial;            // [B*Hq, n_chunks, d + 2]
+    float * out;
+};
+hipError_t launch_attend(const dev_tables & kt, const dev_tables & vt, const attend_args & a,
+                         hipStream_t s);
+int attend_chunk_tokens(int32_t d);
+
+struct scores_args {
+    const float * qp;
+    int64_t qp_stride;
+    int64_t n_q;
+    tq_planes k;
+    int64_t n_k;
+    float scale;
+    int32_t top_k;
+    float * out_scores;
+    int64_t * out_idx;
+    float * cand_s;             // top-k candidates [n_ranges, n_q, top_k]
+    int64_t * cand_i;
+    int32_t n_ranges;
+};
+hipError_t launch_scores(const dev_tables & t, const scores_args & a, hipStream_t s);
+int32_t scores_ranges(int64_t n_k);
+
+}  // namespace tq

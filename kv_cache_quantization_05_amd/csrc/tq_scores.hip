@@ -1,0 +1,316 @@
+// Scores of rotated queries against packed keys, and fused top-k search.
+//
+// s = scale * N * ( <R q, c[code]> / sqrt(d) + gamma sqrt(pi/2)/m <S R q, sigma> )
+// read straight from the codes: the query is rotated once ([TQ+ guide] §5.3,
+// pre-rotate-queries), stays at full precision ([TQ explainer] §2.2.2), and
+// the QJL sign bits enter as +-1 ([TQ explainer] §2.2; [Orión plan] Fase 3).
+// Inner-product search over a database of packed vectors follows the pages'
+// vector-search use ([TQ explainer] §3.4); the score matrix is never stored:
+// each block keeps a running top-k per query in LDS, a final pass merges the
+// per-range lists (ties -> lower index).
+#include <cmath>
+
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+constexpr int kKeys = 256;   // keys per block sub-tile (one per thread)
+constexpr int kQT = 16;      // queries per block
+
+template <int D, int KB, bool QJL>
+__device__ __forceinline__ void score_key(const dev_tables & t, const scores_args & a, const float (*qs)[kQT],
+                                          const float (*us)[kQT], const float * cb, int64_t j,
+                                          float (&out)[kQT]) {
+    const int64_t kv = j * a.k.stride[2];
+    const uint32_t * crow = reinterpret_cast<const uint32_t *>(a.k.codes + kv * (D * KB / 8));
+    float dot[kQT];
+#pragma unroll
+    for (int i = 0; i < kQT; ++i) dot[i] = 0.f;
+#pragma unroll 1
+    for (int bl = 0; bl < D / 32; ++bl) {
+        uint32_t w[KB];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) w[k] = crow[bl * KB + k];
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+            const float cv = cb[block_code<KB>(w, e)];
+#pragma unroll
+            for (int i = 0; i < kQT; ++i) dot[i] = fmaf(qs[bl * 32 + e][i], cv, dot[i]);
+        }
+    }
+    const float n = half_bits_to_float(a.k.norms[kv]);
+    const float inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(D));
+    if constexpr (QJL) {
+        const uint32_t * srow = reinterpret_cast<const uint32_t *>(a.k.signs + kv * (D / 8));
+        float dq[kQT];
+#pragma unroll
+        for (int i = 0; i < kQT; ++i) dq[i] = 0.f;
+#pragma unroll 1
+        for (int bl = 0; bl < D / 32; ++bl) {
+            const uint32_t sw = srow[bl];
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                const float sg = ((sw >> e) & 1) ? 1.f : -1.f;
+#pragma unroll
+                for (int i = 0; i < kQT; ++i) dq[i] = fmaf(us[bl * 32 + e][i], sg, dq[i]);
+            }
+        }
+        const float gam = half_bits_to_float(a.k.rnorms[kv]) * sqrtf(0.5f * static_cast<float>(M_PI)) /
+                          static_cast<float>(D);
+#pragma unroll
+        for (int i = 0; i < kQT; ++i) out[i] = a.scale * n * (dot[i] * inv_sqrt_d + gam * dq[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kQT; ++i) out[i] = a.scale * n * inv_sqrt_d * dot[i];
+    }
+    (void)t;
+}
+
+template <int D, bool QJL>
+__device__ __forceinline__ void load_query_tile(const scores_args & a, int64_t q0, float (*qs)[kQT],
+                                                float (*us)[kQT], int tid) {
+    for (int i = tid; i < kQT * D; i += 256) {
+        const int qi = i / D, e = i % D;
+        const int64_t qq = q0 + qi;
+        const float * row = a.qp + (qq < a.n_q ? qq : a.n_q - 1) * a.qp_stride;
+        qs[e][qi] = row[e];
+        if constexpr (QJL) us[e][qi] = row[D + e];
+    }
+}
+
+template <int D, int KB, bool QJL>
+__global__ __launch_bounds__(256) void scores_full_kernel(const dev_tables t, const scores_args a) {
+    __shared__ __align__(16) float qs[D][kQT];
+    __shared__ __align__(16) float us[QJL ? D : 1][kQT];
+    __shared__ float cb[16];
+    const int tid = threadIdx.x;
+    const int64_t q0 = int64_t(blockIdx.y) * kQT;
+    load_query_tile<D, QJL>(a, q0, qs, us, tid);
+    if (tid < 16) cb[tid] = t.cb[tid];
+    __syncthreads();
+    const int64_t j = int64_t(blockIdx.x) * kKeys + tid;
+    if (j >= a.n_k) return;
+    float s[kQT];
+    score_key<D, KB, QJL>(t, a, qs, us, cb, j, s);
+#pragma unroll
+    for (int i = 0; i < kQT; ++i)
+        if (q0 + i < a.n_q) a.out_scores[(q0 + i) * a.n_k + j] = s[i];
+}
+
+// (score desc, index asc) ordering
+__device__ __forceinline__ bool better(float s1, int64_t i1, float s2, int64_t i2) {
+    return s1 > s2 || (s1 == s2 && i1 < i2);
+}
+
+// One wave merges the candidate scores cs[0..255] (indices ci) of a query into
+// its sorted list (ls, li) of length K, keeping the K best.
+__device__ void wave_merge_topk(float * ls, int64_t * li, int K, const float * cs, const int64_t * ci,
+                                int lane, float * tmp_s, int64_t * tmp_i) {
+    // lane-local candidates: 4 new + list entries k with k % 64 == lane
+    float c_s[5];
+    int64_t c_i[5];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        c_s[r] = cs[lane + 64 * r];
+        c_i[r] = ci[lane + 64 * r];
+    }
+    // the list is at most 64 long -> one entry per lane
+    c_s[4] = lane < K ? ls[lane] : -INFINITY;
+    c_i[4] = lane < K ? li[lane] : INT64_MAX;
+    for (int k = 0; k < K; ++k) {
+        float bs = -INFINITY;
+        int64_t bi = INT64_MAX;
+        int br = -1;
+#pragma unroll
+        for (int r = 0; r < 5; ++r)
+            if (better(c_s[r], c_i[r], bs, bi)) {
+                bs = c_s[r];
+                bi = c_i[r];
+                br = r;
+            }
+        float ws = bs;
+        int64_t wi = bi;
+        for (int o = 32; o > 0; o >>= 1) {
+            float os = __shfl_xor(ws, o);
+            int64_t oi = __shfl_xor(wi, o);
+            if (better(os, oi, ws, wi)) {
+                ws = os;
+                wi = oi;
+            }
+        }
+        // the owner removes the winner (indices are unique among candidates)
+        if (br >= 0 && bi == wi && bs == ws) {
+#pragma unroll
+            for (int r = 0; r < 5; ++r)
+                if (r == br) {
+                    c_s[r] = -INFINITY;
+                    c_i[r] = INT64_MAX;
+                }
+        }
+        if (lane == 0) {
+            tmp_s[k] = ws;
+            tmp_i[k] = wi;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < K) {
+        ls[lane] = tmp_s[lane];
+        li[lane] = tmp_i[lane];
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+template <int D, int KB, bool QJL>
+__global__ __launch_bounds__(256) void scores_topk_kernel(const dev_tables t, const scores_args a) {
+    __shared__ __align__(16) float qs[D][kQT];
+    __shared__ __align__(16) float us[QJL ? D : 1][kQT];
+    __shared__ float cb[16];
+    __shared__ float cand_s[kQT][kKeys];
+    __shared__ float list_s[kQT][64];
+    __shared__ int64_t list_i[kQT][64];
+    __shared__ float tmp_s[4][64];
+    __shared__ int64_t tmp_i[4][64];
+    __shared__ int64_t key_idx[kKeys];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int K = a.top_k;
+    const int64_t q0 = int64_t(blockIdx.y) * kQT;
+    load_query_tile<D, QJL>(a, q0, qs, us, tid);
+    if (tid < 16) cb[tid] = t.cb[tid];
+    for (int i = tid; i < kQT * 64; i += 256) {
+        list_s[i / 64][i % 64] = -INFINITY;
+        list_i[i / 64][i % 64] = INT64_MAX;
+    }
+    const int64_t per = (a.n_k + a.n_ranges - 1) / a.n_ranges;
+    const int64_t k_begin = int64_t(blockIdx.x) * per;
+    const int64_t k_end = k_begin + per < a.n_k ? k_begin + per : a.n_k;
+    __syncthreads();
+    for (int64_t j0 = k_begin; j0 < k_end; j0 += kKeys) {
+        const int64_t j = j0 + tid;
+        float s[kQT];
+        if (j < k_end) {
+            score_key<D, KB, QJL>(t, a, qs, us, cb, j, s);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kQT; ++i) s[i] = -INFINITY;
+        }
+#pragma unroll
+        for (int i = 0; i < kQT; ++i) cand_s[i][tid] = s[i];
+        key_idx[tid] = j < k_end ? j : INT64_MAX;
+        __syncthreads();
+        // wave wv handles queries wv, wv+4, ...
+        for (int qi = wv; qi < kQT; qi += 4) {
+            const float thr = list_s[qi][K - 1];
+            bool any = false;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) any |= cand_s[qi][lane + 64 * r] > thr;
+            if (__any(any)) wave_merge_topk(list_s[qi], list_i[qi], K, cand_s[qi], key_idx, lane, tmp_s[wv], tmp_i[wv]);
+        }
+        __syncthreads();
+    }
+    for (int i = tid; i < kQT * K; i += 256) {
+        const int qi = i / K, k = i % K;
+        const int64_t qq = q0 + qi;
+        if (qq >= a.n_q) continue;
+        const int64_t o = (int64_t(blockIdx.x) * a.n_q + qq) * K + k;
+        a.cand_s[o] = list_s[qi][k];
+        a.cand_i[o] = list_i[qi][k];
+    }
+}
+
+// Final merge: one wave per query over n_ranges sorted lists of length K.
+__global__ __launch_bounds__(64) void topk_merge_kernel(const scores_args a) {
+    const int64_t qq = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int K = a.top_k;
+    // cursor per list: lane owns lists lane, lane+64, ...
+    const int per_lane = (a.n_ranges + 63) / 64;
+    int cur[4];
+    for (int r = 0; r < 4; ++r) cur[r] = 0;
+    for (int k = 0; k < K; ++k) {
+        float bs = -INFINITY;
+        int64_t bi = INT64_MAX;
+        int br = -1;
+        for (int r = 0; r < per_lane && r < 4; ++r) {
+            const int list = lane + 64 * r;
+            if (list >= a.n_ranges || cur[r] >= K) continue;
+            const int64_t o = (int64_t(list) * a.n_q + qq) * K + cur[r];
+            const float s = a.cand_s[o];
+            const int64_t i = a.cand_i[o];
+            if (better(s, i, bs, bi)) {
+                bs = s;
+                bi = i;
+                br = r;
+            }
+        }
+        float ws = bs;
+        int64_t wi = bi;
+        for (int o = 32; o > 0; o >>= 1) {
+            float os = __shfl_xor(ws, o);
+            int64_t oi = __shfl_xor(wi, o);
+            if (better(os, oi, ws, wi)) {
+                ws = os;
+                wi = oi;
+            }
+        }
+        if (br >= 0 && bs == ws && bi == wi) {
+            for (int r = 0; r < 4; ++r)
+                if (r == br) ++cur[r];
+        }
+        if (lane == 0) {
+            a.out_scores[qq * K + k] = ws;
+            a.out_idx[qq * K + k] = wi;
+        }
+    }
+}
+
+template <int D, int KB, bool QJL>
+hipError_t launch_scores_t(const dev_tables & t, const scores_args & a, hipStream_t s) {
+    const int64_t qtiles = (a.n_q + kQT - 1) / kQT;
+    if (a.top_k == 0) {
+        dim3 grid((a.n_k + kKeys - 1) / kKeys, qtiles);
+        hipLaunchKernelGGL((scores_full_kernel<D, KB, QJL>), grid, dim3(256), 0, s, t, a);
+        return hipGetLastError();
+    }
+    dim3 grid(a.n_ranges, qtiles);
+    hipLaunchKernelGGL((scores_topk_kernel<D, KB, QJL>), grid, dim3(256), 0, s, t, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(a.n_q), dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_scores_d(const dev_tables & t, const scores_args & a, hipStream_t s) {
+    switch (t.bits * 2 + (t.qjl ? 1 : 0)) {
+        case 4: return launch_scores_t<D, 2, false>(t, a, s);
+        case 5: return launch_scores_t<D, 2, true>(t, a, s);
+        case 6: return launch_scores_t<D, 3, false>(t, a, s);
+        case 7: return launch_scores_t<D, 3, true>(t, a, s);
+        case 8: return launch_scores_t<D, 4, false>(t, a, s);
+        case 9: return launch_scores_t<D, 4, true>(t, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int32_t scores_ranges(int64_t n_k) {
+    int64_t r = (n_k + 4095) / 4096;
+    if (r > 256) r = 256;
+    if (r < 1) r = 1;
+    return static_cast<int32_t>(r);
+}
+
+hipError_t launch_scores(const dev_tables & t, const scores_args & a, hipStream_t s) {
+    switch (t.d) {
+        case 32: return launch_scores_d<32>(t, a, s);
+        case 64: return launch_scores_d<64>(t, a, s);
+        case 128: return launch_scores_d<128>(t, a, s);
+        case 256: return launch_scores_d<256>(t, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace tq

@@ -1,0 +1,162 @@
+// Host-side table generation for libtq: rotation signs, JL matrix, codebook.
+//
+// Rotation data is generated from the seed at context creation rather than
+// shipped as a static table, and one seed always yields one matrix
+// ([TQ+ guide] §3, Codex finding 6).  Readings where the pages are silent:
+//   * generator: SplitMix64 (Steele, Lea, Flood 2014); it is counter based,
+//     output k of a stream seeded with s is mix(s + (k+1) * golden_gamma);
+//   * D1 = outputs 0..d-1, D2 = outputs d..2d-1 of the stream seeded with the
+//     config seed; the entry is -1 when the output's top bit is set;
+//   * S (m x d, row-major) from the stream seeded with seed ^ 0x514A4C00...;
+//     consecutive output pairs -> Box-Muller (double) -> two float entries;
+//   * codebook: Lloyd-Max quantiser of N(0,1) with 2^b levels (Max 1960),
+//     each centroid rounded once from double to fp16 (RNE); thresholds are
+//     midpoints of neighbouring fp16 centroids (exact in float).
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+constexpr uint64_t kSStream = 0x514A4C0000000000ull;
+
+uint64_t mix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// Output k (0-based) of the SplitMix64 stream seeded with `seed`.
+uint64_t splitmix_at(uint64_t seed, uint64_t k) { return mix64(seed + (k + 1) * kGamma); }
+
+// Round a double to the nearest fp16 (ties to even) in one step.
+uint16_t half_bits_from_double(double v) {
+    uint16_t sign = std::signbit(v) ? 0x8000 : 0;
+    double a = std::fabs(v);
+    if (std::isnan(v)) return 0x7E00;
+    if (a >= 65520.0) return sign | 0x7C00;
+    if (a < std::ldexp(1.0, -14)) {
+        double q = std::nearbyint(std::ldexp(a, 24));  // exact scaling, RNE
+        return sign | static_cast<uint16_t>(q);       // q == 1024 is the min normal
+    }
+    int e2;
+    std::frexp(a, &e2);                                // a = f * 2^e2, f in [0.5, 1)
+    int e = e2 - 1;
+    double q = std::nearbyint(std::ldexp(a, 10 - e));  // in [1024, 2048]
+    if (q >= 2048.0) {
+        q = 1024.0;
+        e += 1;
+    }
+    if (e + 15 >= 31) return sign | 0x7C00;
+    return sign | static_cast<uint16_t>(((e + 15) << 10) | (static_cast<int>(q) - 1024));
+}
+
+double half_bits_to_double(uint16_t h) {
+    int e = (h >> 10) & 31;
+    int f = h & 1023;
+    double v = e == 0 ? std::ldexp(static_cast<double>(f), -24)
+                      : std::ldexp(static_cast<double>(f + 1024), e - 25);
+    return (h & 0x8000) ? -v : v;
+}
+
+double gauss_pdf(double t) {
+    return std::isinf(t) ? 0.0 : std::exp(-0.5 * t * t) / std::sqrt(2.0 * M_PI);
+}
+
+// P(a < X <= b), X ~ N(0,1), using the tail that keeps relative precision.
+double gauss_mass(double a, double b) {
+    const double r2 = std::sqrt(2.0);
+    if (a >= 0.0) return 0.5 * (std::erfc(a / r2) - std::erfc(b / r2));
+    if (b <= 0.0) return 0.5 * (std::erfc(-b / r2) - std::erfc(-a / r2));
+    return 1.0 - 0.5 * std::erfc(-a / r2) - 0.5 * std::erfc(b / r2);
+}
+
+// Lloyd's iteration for the minimum-MSE quantiser of N(0,1).
+std::vector<double> lloyd_max(int bits) {
+    const int L = 1 << bits;
+    std::vector<double> c(L), t(L + 1), nc(L);
+    for (int k = 0; k < L; ++k) c[k] = -3.0 + 6.0 * (k + 0.5) / L;
+    for (int it = 0; it < 100000; ++it) {
+        t[0] = -INFINITY;
+        t[L] = INFINITY;
+        for (int k = 1; k < L; ++k) t[k] = 0.5 * (c[k - 1] + c[k]);
+        double moved = 0.0;
+        for (int k = 0; k < L; ++k) {
+            nc[k] = (gauss_pdf(t[k]) - gauss_pdf(t[k + 1])) / gauss_mass(t[k], t[k + 1]);
+            moved = std::fmax(moved, std::fabs(nc[k] - c[k]));
+        }
+        c.swap(nc);
+        if (moved < 1e-15) break;
+    }
+    return c;
+}
+
+}  // namespace
+
+int validate_config(const tq_config & cfg, const char ** why) {
+    const int d = cfg.head_dim;
+    if (d != 32 && d != 64 && d != 128 && d != 256) {
+        *why = "head_dim must be 32, 64, 128 or 256";
+        return TQ_STATUS_INVALID_ARG;
+    }
+    if (cfg.bits < 2 || cfg.bits > 4) {
+        *why = "bits must be 2, 3 or 4";
+        return TQ_STATUS_INVALID_ARG;
+    }
+    if (cfg.block != 32) {
+        *why = "block must be 32";
+        return TQ_STATUS_INVALID_ARG;
+    }
+    if (cfg.qjl != 0 && cfg.qjl != 1) {
+        *why = "qjl must be 0 or 1";
+        return TQ_STATUS_INVALID_ARG;
+    }
+    if (cfg.qjl_dim < 0 || (cfg.qjl_dim > 0 && (cfg.qjl_dim % 32 != 0 || cfg.qjl_dim > 256))) {
+        *why = "qjl_dim must be 0 or a multiple of 32 up to 256";
+        return TQ_STATUS_INVALID_ARG;
+    }
+    if (cfg.qjl && cfg.qjl_dim != 0 && cfg.qjl_dim != d) {
+        *why = "qjl_dim other than head_dim is not supported by the kernels";
+        return TQ_STATUS_UNSUPPORTED;
+    }
+    return TQ_STATUS_OK;
+}
+
+int build_tables(const tq_config & cfg, int8_t * d1, int8_t * d2, float * codebook,
+                 float * thresholds, float * s_rowmajor) {
+    const int d = cfg.head_dim;
+    const int m = cfg.qjl_dim ? cfg.qjl_dim : d;
+    for (int i = 0; i < d; ++i) {
+        if (d1) d1[i] = (splitmix_at(cfg.seed, i) >> 63) ? -1 : 1;
+        if (d2) d2[i] = (splitmix_at(cfg.seed, d + i) >> 63) ? -1 : 1;
+    }
+    const int L = 1 << cfg.bits;
+    std::vector<double> c = lloyd_max(cfg.bits);
+    std::vector<double> c16(L);
+    for (int k = 0; k < L; ++k) c16[k] = half_bits_to_double(half_bits_from_double(c[k]));
+    // Lloyd's iteration keeps the centroids ascending; rounding preserves order.
+    if (codebook)
+        for (int k = 0; k < L; ++k) codebook[k] = static_cast<float>(c16[k]);
+    if (thresholds)
+        for (int k = 0; k + 1 < L; ++k) thresholds[k] = static_cast<float>(0.5 * (c16[k] + c16[k + 1]));
+    if (cfg.qjl && s_rowmajor) {
+        const uint64_t s_seed = cfg.seed ^ kSStream;
+        const int64_t total = static_cast<int64_t>(m) * d;
+        for (int64_t k = 0; k < total; k += 2) {
+            uint64_t z1 = splitmix_at(s_seed, k);
+            uint64_t z2 = splitmix_at(s_seed, k + 1);
+            double u1 = std::ldexp(static_cast<double>((z1 >> 11) + 1), -53);
+            double u2 = std::ldexp(static_cast<double>(z2 >> 11), -53);
+            double r = std::sqrt(-2.0 * std::log(u1));
+            s_rowmajor[k] = static_cast<float>(r * std::cos(2.0 * M_PI * u2));
+            s_rowmajor[k + 1] = static_cast<float>(r * std::sin(2.0 * M_PI * u2));
+        }
+    }
+    return TQ_STATUS_OK;
+}
+
+}  // namespace tq

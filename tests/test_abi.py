@@ -1,0 +1,81 @@
+"""Host-side checks of libtq: it loads, exports the C ABI, and its host-built
+tables equal the oracle's (no GPU needed: tq_tables_export never touches a
+device)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from kv_cache_quantization_05_amd import binding
+from oracle import tables
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "tq.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.lib()
+    declared = _declared_functions()
+    assert len(declared) >= 10
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(binding.EXPORTED)
+    assert lib.tq_version().decode().startswith("libtq")
+
+
+@pytest.mark.parametrize("seed", [0, 1, 987654321, 2**64 - 1])
+@pytest.mark.parametrize("d", [32, 128, 256])
+def test_rotation_signs_match_oracle(seed, d):
+    t = binding.tables_export(seed=seed, head_dim=d, bits=3)
+    o1, o2 = tables.rotation_signs(seed, d)
+    assert np.array_equal(t["d1"], o1)
+    assert np.array_equal(t["d2"], o2)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_codebook_and_thresholds_match_oracle_bit_exact(bits):
+    t = binding.tables_export(seed=0, head_dim=128, bits=bits)
+    assert np.array_equal(t["codebook"].astype(np.float64), tables.codebook(bits))
+    assert np.array_equal(t["thresholds"].astype(np.float64), tables.thresholds(bits))
+
+
+@pytest.mark.parametrize("seed,d", [(0, 128), (5, 256), (123, 32)])
+def test_qjl_matrix_matches_oracle_bit_exact(seed, d):
+    t = binding.tables_export(seed=seed, head_dim=d, bits=4, qjl=True)
+    S = tables.gaussian_matrix(seed, d, d)
+    assert np.array_equal(t["S"].astype(np.float64), S)
+
+
+def test_sizes_and_config_errors():
+    assert binding.code_bytes(128, 3) == 48
+    assert binding.code_bytes(128, 4) == 64
+    assert binding.code_bytes(256, 4) == 128
+    lib = binding.lib()
+    bad = binding.make_config(0, 100, 3)
+    assert lib.tq_code_bytes(ctypes.byref(bad)) == 0
+    with pytest.raises(binding.TQError) as e:
+        binding.tables_export(seed=0, head_dim=128, bits=5)
+    assert e.value.status == 1 and "bits" in str(e.value)
+    with pytest.raises(binding.TQError):
+        binding.tables_export(seed=0, head_dim=48, bits=3)
+    # a valid call clears the error text
+    binding.tables_export(seed=0, head_dim=64, bits=2)
+    assert lib.tq_last_error() == b""
+    q = binding.make_config(0, 128, 4, qjl=True)
+    assert lib.tq_sign_bytes(ctypes.byref(q)) == 16
+
+
+def test_null_arguments_rejected_without_device():
+    lib = binding.lib()
+    assert lib.tq_ctx_create(None, None) == 1
+    assert lib.tq_encode(None, None, 0, 1, 1, 1, None, binding.Planes(), None) == 1
+    assert b"ctx" in lib.tq_last_error()
+    assert lib.tq_attend_decode_workspace(None, 1, 1, 1, 1) == -1
