@@ -117,6 +117,8 @@ def main():
     ap.add_argument("--workload", default="llama_t32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--min-rotation-bytes", type=float, default=1.1 * 2**30)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one 1 GiB device copy (a known-size reference for memory counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the single-GPU "
@@ -128,6 +130,12 @@ def main():
     from kv_cache_quantization_05_amd import binding as tq
     from kv_cache_quantization_05_amd import workloads as wl
 
+    if args.calibrate_copy:
+        src = torch.ones(2**28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = wl.WORKLOADS[args.workload]
     if w.name == "search_1m":
         raise SystemExit("search_1m is a parity workload; use a decode workload here")
@@ -146,7 +154,7 @@ def main():
     inputs = [(K, V)] + [(K.clone(), V.clone()) for _ in range(R_in - 1)]
     caches = [(kctx.new_planes((w.B, w.Hkv, w.T)), vctx.new_planes((w.B, w.Hkv, w.T))) for _ in range(R_pk)]
     out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
-    ws = torch.empty(tq.attend_workspace_bytes(kctx, w.B, w.Hq, w.Hkv, w.T), dtype=torch.uint8, device=dev)
+    ws = torch.empty(tq.attend_workspace_bytes(kctx, vctx, w.B, w.Hq, w.Hkv, w.T), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     for i in range(R_pk):  # every copy holds a valid encoding before timing
         tq.encode(kctx, inputs[i % R_in][0], caches[i][0])

@@ -19,7 +19,7 @@
  * Errors: arguments are validated on the host before anything is enqueued; a
  * failed check returns a non-zero tq_status and leaves the stream untouched.
  * tq_last_error() then describes it (thread-local).  A failed kernel launch
- * returns TQ_ERR_DEVICE.  Faults inside a kernel surface at the caller's next
+ * returns TQ_STATUS_DEVICE.  Faults inside a kernel surface at the caller's next
  * synchronisation.  NaN/Inf inputs are not checked; their outputs are
  * undefined.  No C++ exception crosses this interface.
  *
@@ -72,7 +72,8 @@ enum tq_dtype {
  *   bits      b: 2, 3 or 4 bits per coordinate
  *   block     32 (codes per packed block)
  *   qjl       1 adds the 1-bit QJL residual sketch ([TQ explainer] §2.2)
- *   qjl_dim   m, rows of S: 0 means m = d; otherwise a multiple of 32, <= 256
+ *   qjl_dim   m, rows of S: 0 means m = d (the kernels support only m = d;
+ *             another multiple of 32 up to 256 gives TQ_STATUS_UNSUPPORTED)
  */
 struct tq_config {
     uint64_t seed;
@@ -130,8 +131,9 @@ int64_t tq_sign_bytes(const struct tq_config * cfg);
  * at x[i0*x_stride[0] + i1*x_stride[1] + i2*x_stride[2] + k] (strides in
  * elements; the d elements of a vector are contiguous and 16-byte aligned).
  * out: planes to write (caller-owned device memory).  n0*n1*n2 == 0 is a no-op.
- * Codes of a coordinate within about 1e-6 of a decision threshold may differ
- * from a float64 evaluation of the same rule.
+ * The rotation and z are evaluated in double precision, so codes and fp16
+ * norms match a float64 evaluation of the same rule except within rounding
+ * distance (~1e-15 relative) of a threshold or of an fp16 rounding midpoint.
  */
 int32_t tq_encode(const struct tq_ctx * ctx, const void * x, int32_t x_dtype,
                   int64_t n0, int64_t n1, int64_t n2, const int64_t x_stride[3],
@@ -178,8 +180,11 @@ int32_t tq_attend_decode(const struct tq_ctx * k_ctx, const struct tq_ctx * v_ct
                          int64_t t_max, float scale, float * out,
                          void * workspace, int64_t workspace_bytes, void * hip_stream);
 
-int64_t tq_attend_decode_workspace(const struct tq_ctx * k_ctx, int32_t B, int32_t Hq,
-                                   int32_t Hkv, int64_t t_max);
+/* Workspace bytes tq_attend_decode needs for these contexts and sizes (the
+ * split of the context into chunks depends on the device's occupancy); -1 on
+ * invalid arguments. */
+int64_t tq_attend_decode_workspace(const struct tq_ctx * k_ctx, const struct tq_ctx * v_ctx, int32_t B,
+                                   int32_t Hq, int32_t Hkv, int64_t t_max);
 
 /* Thread-local description of the last non-OK status ("" if none). */
 const char * tq_last_error(void);

@@ -73,7 +73,7 @@ def lib():
         L.tq_attend_decode.argtypes = [vp, vp, vp, Planes, Planes, vp, i32, i32, i32, i64,
                                        ctypes.c_float, vp, vp, i64, vp]
         L.tq_attend_decode.restype = i32
-        L.tq_attend_decode_workspace.argtypes = [vp, i32, i32, i32, i64]
+        L.tq_attend_decode_workspace.argtypes = [vp, vp, i32, i32, i32, i64]
         L.tq_attend_decode_workspace.restype = i64
         L.tq_last_error.argtypes = []
         L.tq_last_error.restype = ctypes.c_char_p
@@ -241,8 +241,8 @@ def encode(ctx: Context, x: torch.Tensor, planes: PackedPlanes = None, stream=No
     return planes
 
 
-def attend_workspace_bytes(k_ctx, B, Hq, Hkv, t_max):
-    return lib().tq_attend_decode_workspace(k_ctx.handle, B, Hq, Hkv, t_max)
+def attend_workspace_bytes(k_ctx, v_ctx, B, Hq, Hkv, t_max):
+    return lib().tq_attend_decode_workspace(k_ctx.handle, v_ctx.handle, B, Hq, Hkv, t_max)
 
 
 def attend_decode(k_ctx: Context, v_ctx: Context, q: torch.Tensor, k: PackedPlanes, v: PackedPlanes,
@@ -259,7 +259,7 @@ def attend_decode(k_ctx: Context, v_ctx: Context, q: torch.Tensor, k: PackedPlan
         scale = d ** -0.5
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
-    need = attend_workspace_bytes(k_ctx, B, Hq, Hkv, t_max)
+    need = attend_workspace_bytes(k_ctx, v_ctx, B, Hq, Hkv, t_max)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(lib().tq_attend_decode(k_ctx.handle, v_ctx.handle, _ptr(q), k.c_struct(), v.c_struct(),

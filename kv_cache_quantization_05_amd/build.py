@@ -23,7 +23,9 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           f"-I{os.path.join(os.path.dirname(PKG), 'include')}"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-munsafe-fp-atomics"]
+          "-munsafe-fp-atomics",
+          # keep MFMA accumulators in ordinary VGPRs (no AGPR copies in loops)
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc():

@@ -1,325 +1,60 @@
-// Decode attention straight from packed K/V codes.
-//
-//  * query prep: q' = R q once per query head, and u = S q' for QJL keys --
-//    the pre-rotate-queries identity <q, R^T c> = <R q, c> ([TQ+ guide] §5.3)
-//    replaces a d-point inverse rotation per cached position by one rotation
-//    of the query;
-//  * partial kernel (split-K over the context, "flash decoding"): logits from
-//    codes, online softmax, value accumulation in the rotated domain
-//    ([TQ explainer] §4.3 attention; full-precision query §2.2.2);
-//  * merge kernel: log-sum-exp merge of the chunks, then the output is rotated
-//    back, o = R^T o' ([TQ+ guide] §6.1, the inverse-rotation fix).
-#include <cmath>
-
-#include "tq_device.h"
+// Decode attention dispatch: query prep, partial kernels, merge.
 #include "tq_internal.h"
 
 namespace tq {
-namespace {
 
-constexpr int kSub = 256;  // tokens per sub-tile (= threads per block)
+#define TQ_DECLARE_DIM(D)                                                                              \
+    hipError_t launch_attend_dim##D(const dev_tables &, const dev_tables &, const attend_args &, hipStream_t); \
+    hipError_t launch_prep_dim##D(const dev_tables &, const float *, int64_t, float *, int64_t, hipStream_t);
+TQ_DECLARE_DIM(32)
+TQ_DECLARE_DIM(64)
+TQ_DECLARE_DIM(128)
+TQ_DECLARE_DIM(256)
+#undef TQ_DECLARE_DIM
 
-// In-LDS Walsh-Hadamard transform of D floats by D threads (unnormalised).
-template <int D>
-__device__ __forceinline__ void lds_fwht(float * s, int k) {
-#pragma unroll
-    for (int h = 1; h < D; h <<= 1) {
-        __syncthreads();
-        if ((k & h) == 0) {
-            float a = s[k], b = s[k + h];
-            s[k] = a + b;
-            s[k + h] = a - b;
+// Tokens per split-K chunk.  Each (batch, KV head, chunk) is one block; the
+// chunk is a multiple of 128 tokens chosen so that the number of blocks fills
+// whole rounds of the resident block slots (no half-empty last round),
+// preferring the fewest rounds (fewest partial states) that reach 90%.
+int attend_chunk_tokens(const dev_tables & kt, const dev_tables & vt, int32_t B, int32_t Hq, int32_t Hkv,
+                        int64_t t_max) {
+    if (t_max <= 0 || B <= 0 || Hkv <= 0) return 128;
+    static int cu_count = 0;
+    if (cu_count == 0) {
+        int dev = 0;
+        hipDeviceProp_t prop;
+        cu_count = (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+                       ? prop.multiProcessorCount
+                       : 256;
+    }
+    const bool mfma = attend_mfma_shape_ok(kt, vt, Hq, Hkv);
+    const int64_t slots = int64_t(cu_count) * (mfma ? attend_mfma_blocks_per_cu(kt, vt) : 2);
+    const int64_t base = int64_t(B) * Hkv;
+    int64_t best_chunk = 0;
+    double best_eff = -1.0;
+    for (int r = 1; r <= 32; ++r) {
+        const int64_t per_bg = (r * slots + base - 1) / base;
+        int64_t chunk = (t_max + per_bg - 1) / per_bg;
+        chunk = (chunk + 127) / 128 * 128;
+        const int64_t blocks = base * ((t_max + chunk - 1) / chunk);
+        const double eff = double(blocks) / double(((blocks + slots - 1) / slots) * slots);
+        if (eff > best_eff + 1e-9) {
+            best_eff = eff;
+            best_chunk = chunk;
         }
+        if (eff >= 0.9 || chunk <= 256) break;
     }
-    __syncthreads();
-}
-
-template <int D, bool QJL>
-__global__ __launch_bounds__(256) void query_prep_kernel(const dev_tables t, const float * q,
-                                                         float * qp, int64_t stride) {
-    __shared__ float s[D];
-    const int64_t i = blockIdx.x;
-    const int k = threadIdx.x;
-    float x = q[i * D + k];
-    if ((t.d2[k >> 5] >> (k & 31)) & 1) x = -x;
-    s[k] = x;
-    lds_fwht<D>(s, k);
-    float y = s[k] * (1.0f / sqrtf(static_cast<float>(D)));
-    if ((t.d1[k >> 5] >> (k & 31)) & 1) y = -y;
-    qp[i * stride + k] = y;
-    if constexpr (QJL) {
-        __syncthreads();
-        s[k] = y;
-        __syncthreads();
-        // m == d rows of S; row k
-        const float * srow = t.S + int64_t(k) * D;
-        float u = 0.f;
-        for (int e = 0; e < D; ++e) u = fmaf(srow[e], s[e], u);
-        qp[i * stride + D + k] = u;
-    }
-}
-
-template <int D, int KB, int VB, bool QJL, int G>
-__global__ __launch_bounds__(256) void attend_partial_kernel(const dev_tables kt, const dev_tables vt,
-                                                             const attend_args a) {
-    constexpr int VW = VB * D / 32;       // dwords per V code row
-    constexpr int PARTS = 256 / D;        // token partitions in the PV phase
-    __shared__ __align__(16) float qs[D][G];
-    __shared__ __align__(16) float us[QJL ? D : 1][QJL ? G : 1];
-    __shared__ __align__(16) float sc[kSub][G];
-    __shared__ uint32_t vcode[kSub][VW + 1];
-    __shared__ float cbk[16], cbv[16];
-    __shared__ float red[4][G];
-    __shared__ float accred[PARTS][G][D];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wv = tid >> 6;
-    const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    int64_t L = a.seq_lens[b];
-    L = L < 0 ? 0 : (L > a.t_max ? a.t_max : L);
-    const int64_t j_begin = int64_t(chunk) * a.chunk;
-    const int64_t j_end = j_begin + a.chunk < L ? j_begin + a.chunk : L;
-
-    for (int i = tid; i < G * D; i += 256) {
-        const int h = i / D, e = i % D;
-        const float * row = a.qp + (int64_t(b) * a.Hq + g * G + h) * a.qp_stride;
-        qs[e][h] = row[e];
-        if constexpr (QJL) us[e][h] = row[D + e];
-    }
-    if (tid < 16) {
-        cbk[tid] = kt.cb[tid];
-        cbv[tid] = vt.cb[tid];
-    }
-    const int e_dim = tid % D, part = tid / D;
-    float acc[G];
-    float run_m[G], run_l[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        acc[h] = 0.f;
-        run_m[h] = -INFINITY;
-        run_l[h] = 0.f;
-    }
-    const float inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(D));
-    const float qjl_coef = QJL ? sqrtf(0.5f * static_cast<float>(M_PI)) / static_cast<float>(D) : 0.f;
-    const int64_t kb = int64_t(b) * a.k.stride[0] + int64_t(g) * a.k.stride[1];
-    const int64_t vb = int64_t(b) * a.v.stride[0] + int64_t(g) * a.v.stride[1];
-    __syncthreads();
-
-    for (int64_t j0 = j_begin; j0 < j_end; j0 += kSub) {
-        const int64_t j = j0 + tid;
-        const bool valid = j < j_end;
-        float s[G];
-        float wv_norm = 0.f;
-        if (valid) {
-            const int64_t kv = kb + j * a.k.stride[2];
-            const uint32_t * crow = reinterpret_cast<const uint32_t *>(a.k.codes + kv * (D * KB / 8));
-            float dot[G];
-#pragma unroll
-            for (int h = 0; h < G; ++h) dot[h] = 0.f;
-#pragma unroll
-            for (int bl = 0; bl < D / 32; ++bl) {
-                uint32_t w[KB];
-#pragma unroll
-                for (int k = 0; k < KB; ++k) w[k] = crow[bl * KB + k];
-#pragma unroll
-                for (int i = 0; i < 32; ++i) {
-                    const float cv = cbk[block_code<KB>(w, i)];
-#pragma unroll
-                    for (int h = 0; h < G; ++h) dot[h] = fmaf(qs[bl * 32 + i][h], cv, dot[h]);
-                }
-            }
-            const float nk = half_bits_to_float(a.k.norms[kv]);
-            if constexpr (QJL) {
-                const uint32_t * srow = reinterpret_cast<const uint32_t *>(a.k.signs + kv * (D / 8));
-                float dq[G];
-#pragma unroll
-                for (int h = 0; h < G; ++h) dq[h] = 0.f;
-#pragma unroll
-                for (int bl = 0; bl < D / 32; ++bl) {
-                    const uint32_t sw = srow[bl];
-#pragma unroll
-                    for (int i = 0; i < 32; ++i) {
-                        const float sg = ((sw >> i) & 1) ? 1.f : -1.f;
-#pragma unroll
-                        for (int h = 0; h < G; ++h) dq[h] = fmaf(us[bl * 32 + i][h], sg, dq[h]);
-                    }
-                }
-                const float gam = half_bits_to_float(a.k.rnorms[kv]);
-#pragma unroll
-                for (int h = 0; h < G; ++h)
-                    s[h] = a.scale * nk * (dot[h] * inv_sqrt_d + gam * qjl_coef * dq[h]);
-            } else {
-#pragma unroll
-                for (int h = 0; h < G; ++h) s[h] = a.scale * nk * inv_sqrt_d * dot[h];
-            }
-            const int64_t vv = vb + j * a.v.stride[2];
-            wv_norm = half_bits_to_float(a.v.norms[vv]) * inv_sqrt_d;
-            const uint32_t * vrow = reinterpret_cast<const uint32_t *>(a.v.codes + vv * (D * VB / 8));
-#pragma unroll
-            for (int k = 0; k < VW; ++k) vcode[tid][k] = vrow[k];
-        } else {
-#pragma unroll
-            for (int h = 0; h < G; ++h) s[h] = -INFINITY;
-#pragma unroll
-            for (int k = 0; k < VW; ++k) vcode[tid][k] = 0;
-        }
-        // sub-tile max per head
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float m = wave_max(s[h]);
-            if (lane == 0) red[wv][h] = m;
-        }
-        __syncthreads();
-        float scale_old[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float m = fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h]));
-            float new_m = fmaxf(run_m[h], m);
-            scale_old[h] = run_m[h] == -INFINITY ? 0.f : __expf(run_m[h] - new_m);
-            run_m[h] = new_m;
-            float p = valid ? __expf(s[h] - new_m) : 0.f;
-            sc[tid][h] = p * wv_norm;
-            s[h] = p;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float sum = wave_sum(s[h]);
-            if (lane == 0) red[wv][h] = sum;
-        }
-        // PV: dim e_dim over tokens part, part + PARTS, ...
-        float pv[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) pv[h] = 0.f;
-        const int bit = VB * e_dim;
-        const int wi = bit >> 5, off = bit & 31;
-        for (int jj = part; jj < kSub; jj += PARTS) {
-            uint32_t c = vcode[jj][wi] >> off;
-            if (off + VB > 32) c |= vcode[jj][wi + 1] << (32 - off);
-            const float cv = cbv[c & ((1u << VB) - 1)];
-#pragma unroll
-            for (int h = 0; h < G; ++h) pv[h] = fmaf(sc[jj][h], cv, pv[h]);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float sum = red[0][h] + red[1][h] + red[2][h] + red[3][h];
-            run_l[h] = run_l[h] * scale_old[h] + sum;
-            acc[h] = acc[h] * scale_old[h] + pv[h];
-        }
-        __syncthreads();
-    }
-
-    // combine token partitions and write the chunk's partial state
-#pragma unroll
-    for (int h = 0; h < G; ++h) accred[part][h][e_dim] = acc[h];
-    __syncthreads();
-    for (int i = tid; i < G * D; i += 256) {
-        const int h = i / D, e = i % D;
-        float v = 0.f;
-#pragma unroll
-        for (int p = 0; p < PARTS; ++p) v += accred[p][h][e];
-        float * dst = a.partial + ((int64_t(b) * a.Hq + g * G + h) * a.n_chunks + chunk) * (D + 2);
-        dst[2 + e] = v;
-        if (e == 0) {
-            dst[0] = run_m[h];
-            dst[1] = run_l[h];
-        }
-    }
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void attend_merge_kernel(const dev_tables vt, const attend_args a) {
-    __shared__ float s[D];
-    const int h = blockIdx.x, b = blockIdx.y;
-    const int k = threadIdx.x;
-    const float * base = a.partial + (int64_t(b) * a.Hq + h) * a.n_chunks * (D + 2);
-    float M = -INFINITY;
-    for (int c = 0; c < a.n_chunks; ++c) M = fmaxf(M, base[int64_t(c) * (D + 2)]);
-    float o = 0.f;
-    if (M != -INFINITY) {
-        float l = 0.f, acc = 0.f;
-        for (int c = 0; c < a.n_chunks; ++c) {
-            const float * p = base + int64_t(c) * (D + 2);
-            const float w = __expf(p[0] - M);
-            l = fmaf(p[1], w, l);
-            acc = fmaf(p[2 + k], w, acc);
-        }
-        o = acc / l;
-    }
-    // o_orig = R^T o = D2 . H . D1 . o / sqrt(d)
-    if ((vt.d1[k >> 5] >> (k & 31)) & 1) o = -o;
-    s[k] = o;
-    lds_fwht<D>(s, k);
-    float y = s[k] * (1.0f / sqrtf(static_cast<float>(D)));
-    if ((vt.d2[k >> 5] >> (k & 31)) & 1) y = -y;
-    a.out[(int64_t(b) * a.Hq + h) * D + k] = y;
-}
-
-template <int D, int KB, int VB, bool QJL>
-hipError_t launch_attend_g(const dev_tables & kt, const dev_tables & vt, const attend_args & a,
-                           hipStream_t s) {
-    const dim3 grid(a.n_chunks, a.Hkv, a.B);
-    switch (a.Hq / a.Hkv) {
-        case 1: hipLaunchKernelGGL((attend_partial_kernel<D, KB, VB, QJL, 1>), grid, dim3(256), 0, s, kt, vt, a); break;
-        case 2: hipLaunchKernelGGL((attend_partial_kernel<D, KB, VB, QJL, 2>), grid, dim3(256), 0, s, kt, vt, a); break;
-        case 4: hipLaunchKernelGGL((attend_partial_kernel<D, KB, VB, QJL, 4>), grid, dim3(256), 0, s, kt, vt, a); break;
-        case 8: hipLaunchKernelGGL((attend_partial_kernel<D, KB, VB, QJL, 8>), grid, dim3(256), 0, s, kt, vt, a); break;
-        default: return hipErrorInvalidValue;
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attend_merge_kernel<D>), dim3(a.Hq, a.B), dim3(D), 0, s, vt, a);
-    return hipGetLastError();
-}
-
-template <int D, int KB>
-hipError_t launch_attend_kb(const dev_tables & kt, const dev_tables & vt, const attend_args & a,
-                            hipStream_t s) {
-    switch (vt.bits) {
-        case 2: return kt.qjl ? launch_attend_g<D, KB, 2, true>(kt, vt, a, s) : launch_attend_g<D, KB, 2, false>(kt, vt, a, s);
-        case 3: return kt.qjl ? launch_attend_g<D, KB, 3, true>(kt, vt, a, s) : launch_attend_g<D, KB, 3, false>(kt, vt, a, s);
-        case 4: return kt.qjl ? launch_attend_g<D, KB, 4, true>(kt, vt, a, s) : launch_attend_g<D, KB, 4, false>(kt, vt, a, s);
-    }
-    return hipErrorInvalidValue;
-}
-
-template <int D>
-hipError_t launch_attend_d(const dev_tables & kt, const dev_tables & vt, const attend_args & a,
-                           hipStream_t s) {
-    switch (kt.bits) {
-        case 2: return launch_attend_kb<D, 2>(kt, vt, a, s);
-        case 3: return launch_attend_kb<D, 3>(kt, vt, a, s);
-        case 4: return launch_attend_kb<D, 4>(kt, vt, a, s);
-    }
-    return hipErrorInvalidValue;
-}
-
-template <int D>
-hipError_t launch_prep_d(const dev_tables & t, const float * q, int64_t n, float * qp, int64_t stride,
-                         hipStream_t s) {
-    if (t.qjl)
-        hipLaunchKernelGGL((query_prep_kernel<D, true>), dim3(n), dim3(D), 0, s, t, q, qp, stride);
-    else
-        hipLaunchKernelGGL((query_prep_kernel<D, false>), dim3(n), dim3(D), 0, s, t, q, qp, stride);
-    return hipGetLastError();
-}
-
-}  // namespace
-
-int attend_chunk_tokens(int32_t d) {
-    (void)d;
-    return 1024;
+    return static_cast<int>(best_chunk);
 }
 
 hipError_t launch_query_prep(const dev_tables & t, const float * q, int64_t n, float * qp,
                              int64_t qp_stride, hipStream_t s) {
     if (n == 0) return hipSuccess;
     switch (t.d) {
-        case 32: return launch_prep_d<32>(t, q, n, qp, qp_stride, s);
-        case 64: return launch_prep_d<64>(t, q, n, qp, qp_stride, s);
-        case 128: return launch_prep_d<128>(t, q, n, qp, qp_stride, s);
-        case 256: return launch_prep_d<256>(t, q, n, qp, qp_stride, s);
+        case 32: return launch_prep_dim32(t, q, n, qp, qp_stride, s);
+        case 64: return launch_prep_dim64(t, q, n, qp, qp_stride, s);
+        case 128: return launch_prep_dim128(t, q, n, qp, qp_stride, s);
+        case 256: return launch_prep_dim256(t, q, n, qp, qp_stride, s);
     }
     return hipErrorInvalidValue;
 }
@@ -327,10 +62,10 @@ hipError_t launch_query_prep(const dev_tables & t, const float * q, int64_t n, f
 hipError_t launch_attend(const dev_tables & kt, const dev_tables & vt, const attend_args & a,
                          hipStream_t s) {
     switch (kt.d) {
-        case 32: return launch_attend_d<32>(kt, vt, a, s);
-        case 64: return launch_attend_d<64>(kt, vt, a, s);
-        case 128: return launch_attend_d<128>(kt, vt, a, s);
-        case 256: return launch_attend_d<256>(kt, vt, a, s);
+        case 32: return launch_attend_dim32(kt, vt, a, s);
+        case 64: return launch_attend_dim64(kt, vt, a, s);
+        case 128: return launch_attend_dim128(kt, vt, a, s);
+        case 256: return launch_attend_dim256(kt, vt, a, s);
     }
     return hipErrorInvalidValue;
 }

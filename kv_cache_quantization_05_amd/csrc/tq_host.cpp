@@ -221,12 +221,11 @@ int32_t tq_scores(const tq_ctx * k_ctx, const float * q, int64_t n_q, float scal
     return device_status(tq::launch_scores(k_ctx->tab, a, s), "scores launch");
 }
 
-int64_t tq_attend_decode_workspace(const tq_ctx * k_ctx, int32_t B, int32_t Hq, int32_t Hkv,
-                                   int64_t t_max) {
-    if (!k_ctx || B < 0 || Hq < 0 || Hkv <= 0 || t_max < 0) return -1;
-    (void)Hkv;
+int64_t tq_attend_decode_workspace(const tq_ctx * k_ctx, const tq_ctx * v_ctx, int32_t B, int32_t Hq,
+                                   int32_t Hkv, int64_t t_max) {
+    if (!k_ctx || !v_ctx || B < 0 || Hq < 0 || Hkv <= 0 || t_max < 0) return -1;
     const int d = k_ctx->tab.d;
-    const int64_t chunk = tq::attend_chunk_tokens(d);
+    const int64_t chunk = tq::attend_chunk_tokens(k_ctx->tab, v_ctx->tab, B, Hq, Hkv, t_max);
     const int64_t n_chunks = t_max > 0 ? (t_max + chunk - 1) / chunk : 1;
     const int64_t qp = round_up(int64_t(B) * Hq * (d + k_ctx->tab.m) * 4);
     const int64_t part = round_up(int64_t(B) * Hq * n_chunks * (d + 2) * 4);
@@ -255,7 +254,7 @@ int32_t tq_attend_decode(const tq_ctx * k_ctx, const tq_ctx * v_ctx, const float
     if (const char * why = check_planes(k_ctx, k, k_ctx->cfg.qjl != 0))
         return fail(TQ_STATUS_INVALID_ARG, "k: %s", why);
     if (const char * why = check_planes(v_ctx, v, false)) return fail(TQ_STATUS_INVALID_ARG, "v: %s", why);
-    const int64_t need = tq_attend_decode_workspace(k_ctx, B, Hq, Hkv, t_max);
+    const int64_t need = tq_attend_decode_workspace(k_ctx, v_ctx, B, Hq, Hkv, t_max);
     if (!workspace || workspace_bytes < need)
         return fail(TQ_STATUS_INVALID_ARG, "workspace too small: need %lld bytes", (long long)need);
     if (!aligned(workspace, 256)) return fail(TQ_STATUS_INVALID_ARG, "workspace must be 256-byte aligned");
@@ -276,7 +275,7 @@ int32_t tq_attend_decode(const tq_ctx * k_ctx, const tq_ctx * v_ctx, const float
     a.Hq = Hq;
     a.Hkv = Hkv;
     a.t_max = t_max;
-    a.chunk = tq::attend_chunk_tokens(d);
+    a.chunk = tq::attend_chunk_tokens(k_ctx->tab, v_ctx->tab, B, Hq, Hkv, t_max);
     a.n_chunks = t_max > 0 ? static_cast<int32_t>((t_max + a.chunk - 1) / a.chunk) : 1;
     a.scale = scale;
     a.partial = reinterpret_cast<float *>(ws + round_up(int64_t(B) * Hq * qp_stride * 4));

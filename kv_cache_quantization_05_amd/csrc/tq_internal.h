@@ -59,7 +59,14 @@ struct attend_args {
 };
 hipError_t launch_attend(const dev_tables & kt, const dev_tables & vt, const attend_args & a,
                          hipStream_t s);
-int attend_chunk_tokens(int32_t d);
+// Matrix-core partial kernel for d = 128 with 4 query heads per KV head.
+bool attend_mfma_supported(const dev_tables & kt, const dev_tables & vt, const attend_args & a);
+bool attend_mfma_shape_ok(const dev_tables & kt, const dev_tables & vt, int32_t Hq, int32_t Hkv);
+int attend_mfma_blocks_per_cu(const dev_tables & kt, const dev_tables & vt);
+hipError_t launch_attend_mfma_partial(const dev_tables & kt, const dev_tables & vt, const attend_args & a,
+                                      hipStream_t s);
+int attend_chunk_tokens(const dev_tables & kt, const dev_tables & vt, int32_t B, int32_t Hq, int32_t Hkv,
+                        int64_t t_max);
 
 struct scores_args {
     const float * qp;

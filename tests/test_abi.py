@@ -78,4 +78,4 @@ def test_null_arguments_rejected_without_device():
     assert lib.tq_ctx_create(None, None) == 1
     assert lib.tq_encode(None, None, 0, 1, 1, 1, None, binding.Planes(), None) == 1
     assert b"ctx" in lib.tq_last_error()
-    assert lib.tq_attend_decode_workspace(None, 1, 1, 1, 1) == -1
+    assert lib.tq_attend_decode_workspace(None, None, 1, 1, 1, 1) == -1
