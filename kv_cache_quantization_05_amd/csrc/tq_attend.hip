@@ -13,12 +13,12 @@ TQ_DECLARE_DIM(256)
 #undef TQ_DECLARE_DIM
 
 // Tokens per split-K chunk.  Each (batch, KV head, chunk) is one block; the
-// chunk is a multiple of 128 tokens chosen so that the number of blocks fills
+// chunk is a multiple of 256 tokens chosen so that the number of blocks fills
 // whole rounds of the resident block slots (no half-empty last round),
 // preferring the fewest rounds (fewest partial states) that reach 90%.
 int attend_chunk_tokens(const dev_tables & kt, const dev_tables & vt, int32_t B, int32_t Hq, int32_t Hkv,
                         int64_t t_max) {
-    if (t_max <= 0 || B <= 0 || Hkv <= 0) return 128;
+    if (t_max <= 0 || B <= 0 || Hkv <= 0) return 256;
     static int cu_count = 0;
     if (cu_count == 0) {
         int dev = 0;
@@ -35,7 +35,7 @@ int attend_chunk_tokens(const dev_tables & kt, const dev_tables & vt, int32_t B,
     for (int r = 1; r <= 32; ++r) {
         const int64_t per_bg = (r * slots + base - 1) / base;
         int64_t chunk = (t_max + per_bg - 1) / per_bg;
-        chunk = (chunk + 127) / 128 * 128;
+        chunk = (chunk + 255) / 256 * 256;
         const int64_t blocks = base * ((t_max + chunk - 1) / chunk);
         const double eff = double(blocks) / double(((blocks + slots - 1) / slots) * slots);
         if (eff > best_eff + 1e-9) {

@@ -1,14 +1,18 @@
 // Fused decode attention on matrix cores, d = 128, 4 query heads per KV head.
 //
-// The grouped queries sharing one KV head form a real dense contraction
-// against the dequantised codes, so both products run on MFMA
-// (v_mfma_f32_16x16x32_f16):
-//   logits   S[h, j] = sum_i q'[h, i] c[code_ji]   (rows: 4 heads as fp16 hi
-//            parts + 4 heads as fp16 lo parts, so q' keeps ~22 bits; columns:
-//            16 tokens; k: the 32 codes of one block per lane group);
-//   values   O[h, i] += sum_j w[h, j] c[code_ji]   (k = 32 tokens; the
-//            dequantised V tile goes through LDS and comes back transposed
-//            with ds_read_b64_tr_b16).
+// The 4 grouped queries sharing one KV head form a real dense contraction
+// against the dequantised codes, so both products run on the 16-block 4x4x4
+// fp16 MFMA (v_mfma_f32_4x4x4_16b_f16), whose 4-row blocks match the 4 heads
+// exactly (no padded rows):
+//   logits  S[h, t] = sum_i q'[h, i] c[code_ti]: block b covers tokens
+//           4b..4b+3, so lane l ends up holding the 4 head logits of token l;
+//           k runs over 4 dims per instruction, 32 instructions per 128 dims;
+//           the query operand is broadcast from one block (CBSZ/ABID), so each
+//           lane stores query values for only 2 of the 32 k-steps.  q' is split
+//           into fp16 hi + lo parts (two instructions), ~22 bits of precision.
+//   values  O[h, i] += sum_t w[h, t] c[code_ti]: k runs over 4 tokens, block b
+//           covers 4 dims; the dequantised V tile goes through LDS and comes
+//           back transposed with ds_read_b64_tr_b16, as do the weights.
 // Query rotation once per head ([TQ+ guide] §5.3), online softmax
 // ([TQ explainer] §4.3), the output stays in the rotated domain until the
 // merge kernel rotates it back ([TQ+ guide] §6.1).
@@ -17,12 +21,12 @@
 // per-lane offsets are fixed and whose per-step offset is one scalar; the
 // resource's size is the (batch, head)'s valid length, so positions past it
 // read as zero.  The next step's codes are loaded while the current one is
-// unpacked (ping-pong registers).
+// processed (ping-pong register sets, unconditional loads).
 //
 // Softmax bookkeeping per wave: a wave-uniform reference m per head, raised
-// only when s + ln(N_v/sqrt d) exceeds it by more than kSlack (so most steps
-// need no cross-lane max).  p = exp(s - m) feeds the row sum; the PV weight
-// w = p * N_v/sqrt(d) <= e^kSlack stays safe in fp16 whatever the norms.
+// only when a weight w = exp(s - m) * N_v/sqrt(d) would exceed e^kSlack (so
+// most steps need no cross-lane max); w stays safe in fp16 whatever the
+// norms, and the row sum accumulates exp(s - m) in fp32.
 #include <cmath>
 
 #include "tq_device.h"
@@ -32,90 +36,121 @@
 namespace tq {
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;
 constexpr int kG = 4;
-constexpr int kStep = 32;                  // tokens per wave iteration
+constexpr int kStep = 64;                  // tokens per wave iteration (one per lane)
+constexpr int kHalf = 32;                  // tokens per V tile pass
 constexpr int kVRow = 2 * kD + 32;         // bytes per token row of the V tile (padded)
-constexpr int kVTile = kStep * kVRow;      // 9216 B
-constexpr int kPRow = 32;                  // 16 heads x fp16
-constexpr int kPTile = kStep * kPRow;      // 1024 B
+constexpr int kVTile = kHalf * kVRow;      // 9216 B
+constexpr int kPTile = kStep * 8;          // 64 tokens x 4 heads x fp16
 constexpr int kWaveLds = kVTile + kPTile;
 constexpr float kSlack = 4.0f;
 constexpr int kRsrcWord3 = 0x00020000;
 
-__device__ __forceinline__ half8 as_half8(const uint32_t * d) {
-    half8 h;
-    __builtin_memcpy(&h, d, 16);
+// Byte offset of token row r in a wave's V tile: rows are 288 B apart, with
+// 16 B more for rows with bit 2 set.  The 8 rows written together by 16-byte
+// stores start in 8 distinct 16-byte bank slots, and the 4 rows read together
+// by ds_read_b64_tr_b16 cover 128 bytes of banks exactly once; offsets stay
+// affine in the column, so they fold into instruction offsets.
+__device__ __forceinline__ int vrow_off(int r) { return r * kVRow + ((r >> 2) & 1) * 16; }
+
+__device__ __forceinline__ half4 tr_read4(const uint8_t * lds_base, int off) {
+    const shortx4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(lds_base + off));
+    half4 h;
+    __builtin_memcpy(&h, &a, 8);
     return h;
 }
 
-// Byte offset of token row r in a wave's V tile: rows are 288 B apart, with
-// 16 B more for rows with bit 2 set.  The 8 rows written together by
-// 16-byte stores start in 8 distinct 16-byte bank slots, and the 4 rows read
-// together by ds_read_b64_tr_b16 cover the 128 bytes of banks exactly once;
-// offsets stay affine in the column, so they fold into instruction offsets.
-__device__ __forceinline__ int vrow_off(int r) { return r * kVRow + ((r >> 2) & 1) * 16; }
-
-__device__ __forceinline__ half8 tr_read(const uint8_t * lds_base, int off0, int off1) {
-    const shortx4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(lds_base + off0));
-    const shortx4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(lds_base + off1));
-    half8 h;
-    __builtin_memcpy(&h, &a, 8);
-    __builtin_memcpy(reinterpret_cast<char *>(&h) + 8, &b, 8);
+__device__ __forceinline__ half4 as_half4(uint32_t lo, uint32_t hi) {
+    const u32x2 v = {lo, hi};
+    half4 h;
+    __builtin_memcpy(&h, &v, 8);
     return h;
+}
+
+// 4x4x4 MFMA whose A operand comes from block `abid` for all 16 blocks
+// (CBSZ = 4).  abid must fold to a constant once the caller's loops unroll.
+template <int ABID>
+__device__ __forceinline__ floatx4 mfma4_bcast_t(half4 a, half4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 4, ABID, 0);
+}
+
+__device__ __forceinline__ floatx4 mfma4_bcast(int abid, half4 a, half4 b, floatx4 c) {
+    switch (abid) {
+        case 0: return mfma4_bcast_t<0>(a, b, c);
+        case 1: return mfma4_bcast_t<1>(a, b, c);
+        case 2: return mfma4_bcast_t<2>(a, b, c);
+        case 3: return mfma4_bcast_t<3>(a, b, c);
+        case 4: return mfma4_bcast_t<4>(a, b, c);
+        case 5: return mfma4_bcast_t<5>(a, b, c);
+        case 6: return mfma4_bcast_t<6>(a, b, c);
+        case 7: return mfma4_bcast_t<7>(a, b, c);
+        case 8: return mfma4_bcast_t<8>(a, b, c);
+        case 9: return mfma4_bcast_t<9>(a, b, c);
+        case 10: return mfma4_bcast_t<10>(a, b, c);
+        case 11: return mfma4_bcast_t<11>(a, b, c);
+        case 12: return mfma4_bcast_t<12>(a, b, c);
+        case 13: return mfma4_bcast_t<13>(a, b, c);
+        case 14: return mfma4_bcast_t<14>(a, b, c);
+        default: return mfma4_bcast_t<15>(a, b, c);
+    }
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void * base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), kRsrcWord3);
 }
 
-// BITS dwords of one 32-code block at byte offset voff + soff.
-template <int BITS>
-__device__ __forceinline__ void buf_block(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t * w) {
-    if constexpr (BITS == 2) {
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-        w[0] = v.x;
-        w[1] = v.y;
-    } else if constexpr (BITS == 3) {
-        const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0);
-        w[0] = v.x;
-        w[1] = v.y;
-        w[2] = v.z;
-    } else {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-        w[0] = v.x;
-        w[1] = v.y;
-        w[2] = v.z;
-        w[3] = v.w;
+// N consecutive dwords at byte offset voff + soff (N even).
+template <int N>
+__device__ __forceinline__ void buf_dwords(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t * w) {
+    int k = 0;
+#pragma unroll
+    for (; k + 4 <= N; k += 4) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 4 * k, soff, 0);
+        w[k] = v.x;
+        w[k + 1] = v.y;
+        w[k + 2] = v.z;
+        w[k + 3] = v.w;
+    }
+    if constexpr (N % 4 == 2) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff + 4 * (N - 2), soff, 0);
+        w[N - 2] = v.x;
+        w[N - 1] = v.y;
     }
 }
 
 template <int KB, int VB, bool QJL>
 struct step_regs {
-    uint32_t kw[2][KB];   // K block (lane group) of token tile 0 / 1
-    uint32_t vw[2][VB];   // V blocks (lane >> 5) and (lane >> 5) + 2 of token lane & 31
-    uint32_t ks[2];       // QJL sign words
-    uint16_t kr[2];       // QJL residual norms
-    uint16_t nk, nv;      // K and V norms of token lane & 31
+    uint32_t kw[4 * KB];     // K code row of token lane (4 blocks)
+    uint32_t vw[2][2 * VB];  // V blocks 2(lane>>5), 2(lane>>5)+1 of tokens (lane&31), 32+(lane&31)
+    uint32_t ks[QJL ? 4 : 1];
+    uint16_t kr;             // QJL residual norm
+    uint16_t nk, nv;         // K and V norms of token lane
 };
 
+// Waves per SIMD the register budget is sized for: 4 (at most 128 VGPRs) where
+// the loop still fits without spilling, else the compiler's choice.
 template <int KB, int VB, bool QJL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3, QJL ? 2 : 3))) void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
-                                                             const attend_args a) {
+constexpr int waves_per_simd() {
+    return (KB + VB <= 6 && KB != 4 && VB != 4 && (!QJL || KB + VB == 4)) ? 4 : 1;
+}
+
+template <int KB, int VB, bool QJL>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, 256), amdgpu_waves_per_eu(waves_per_simd<KB, VB, QJL>())))
+void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
+                                                          const attend_args a) {
     constexpr uint32_t kKcb = kD * KB / 8, kVcb = kD * VB / 8;
     __shared__ __align__(16) uint8_t lds[4 * kWaveLds];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int lane = tid & 63;
-    const int lrow = lane & 15, lgrp = lane >> 4;
     const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     uint8_t * vtile = lds + wave * kWaveLds;
     uint8_t * ptile = vtile + kVTile;
@@ -126,27 +161,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
     const int64_t w_begin = int64_t(chunk) * a.chunk + wave * wspan;
     const int64_t w_end = w_begin + wspan < L ? w_begin + wspan : L;
 
-    // ---- query operands: rows 0..3 = fp16 hi part of heads 0..3, rows 4..7 = lo part
-    half8 aq[4];
-    half8 au[4];
+    // ---- query operands.  K-step gs (0..31) covers dims of block gs/8 at
+    // positions 4(gs%8)..+3; its query comes from block gs%16, i.e. lanes
+    // 4(gs%16)..+3 (row = head).  This lane sources k-steps lane/4 and lane/4+16.
+    half4 aq[2][2], au[2][2];
     {
-        const int h = lrow & 3;
-        const bool lo = (lrow >> 2) == 1;
-        const float live = lrow < 8 ? 1.f : 0.f;
+        const int h = lane & 3;
         const float * qrow = a.qp + (int64_t(b) * a.Hq + g * kG + h) * a.qp_stride;
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
+        for (int set = 0; set < 2; ++set) {
+            const int gs = (lane >> 2) + 16 * set;
+            const int bl = gs >> 3, kk = gs & 7;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int dim = 32 * lgrp + block_code_of_pos<KB>(8 * mi + i);
-                const float x = live * qrow[dim];
+            for (int i = 0; i < 4; ++i) {
+                const float x = qrow[32 * bl + block_code_of_pos<KB>(4 * kk + i)];
                 const _Float16 hi = static_cast<_Float16>(x);
-                aq[mi][i] = lo ? static_cast<_Float16>(x - static_cast<float>(hi)) : hi;
+                aq[set][0][i] = hi;
+                aq[set][1][i] = static_cast<_Float16>(x - static_cast<float>(hi));
                 if constexpr (QJL) {
-                    const int sdim = 32 * lgrp + sign_bit_of_pos(8 * mi + i);
-                    const float u = live * qrow[kD + sdim];
+                    const float u = qrow[kD + 32 * bl + sign_bit_of_pos(4 * kk + i)];
                     const _Float16 uh = static_cast<_Float16>(u);
-                    au[mi][i] = lo ? static_cast<_Float16>(u - static_cast<float>(uh)) : uh;
+                    au[set][0][i] = uh;
+                    au[set][1][i] = static_cast<_Float16>(u - static_cast<float>(uh));
                 }
             }
         }
@@ -156,17 +192,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
     const float inv_sqrt_d = 1.0f / sqrtf(float(kD));
     const float kscale = a.scale * inv_sqrt_d;
     const float qjl_gain = sqrtf(0.5f * float(M_PI)) / float(kD) * sqrtf(float(kD));
+    const float w_cap = __expf(kSlack);
 
-    // heads 4..15 of the weight tile stay zero
-    if (lane < 32) {
-        uint32_t * pr = reinterpret_cast<uint32_t *>(ptile + lane * kPRow);
-#pragma unroll
-        for (int k = 2; k < 8; ++k) pr[k] = 0;
-    }
-
-    floatx4 acc[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    floatx4 acc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
     float mref[kG], lsum[kG];
 #pragma unroll
     for (int h = 0; h < kG; ++h) {
@@ -190,149 +218,150 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
         rkr = make_rsrc(a.k.rnorms + kvec, Lu * ks2 * 2);
     }
     // per-lane byte offsets relative to the step's first token
-    uint32_t vo_k[2], vo_ks[2], vo_kr[2];
+    const uint32_t vo_k = uint32_t(lane) * ks2 * kKcb;
+    const uint32_t vo_kn = uint32_t(lane) * ks2 * 2;
+    const uint32_t vo_ks = uint32_t(lane) * ks2 * (kD / 8);
+    const uint32_t vo_vn = uint32_t(lane) * vs2 * 2;
+    uint32_t vo_v[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const uint32_t tok = 16 * t + lrow;
-        vo_k[t] = tok * ks2 * kKcb + lgrp * 4 * KB;
-        vo_ks[t] = tok * ks2 * (kD / 8) + lgrp * 4;
-        vo_kr[t] = tok * ks2 * 2;
-    }
-    const uint32_t own_tok = lane & 31;
-    const uint32_t vo_kn = own_tok * ks2 * 2;
-    const uint32_t vo_vn = own_tok * vs2 * 2;
-    const uint32_t vo_v0 = own_tok * vs2 * kVcb + (lane >> 5) * 4 * VB;
-    const uint32_t vo_v1 = vo_v0 + 2 * 4 * VB;
+    for (int h2 = 0; h2 < 2; ++h2)
+        vo_v[h2] = uint32_t(kHalf * h2 + (lane & 31)) * vs2 * kVcb + (lane >> 5) * 8 * VB;
 
     using regs = step_regs<KB, VB, QJL>;
     auto load_step = [&](int64_t j0, regs & r) {
-        const uint32_t j = static_cast<uint32_t>(j0);
-        const uint32_t sk = j * ks2 * kKcb, sv = j * vs2 * kVcb;
+        const uint32_t j = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(j0));  // wave-uniform
+        buf_dwords<4 * KB>(rk, vo_k, j * ks2 * kKcb, r.kw);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            buf_block<KB>(rk, vo_k[t], sk, r.kw[t]);
-            if constexpr (QJL) {
-                r.ks[t] = __builtin_amdgcn_raw_buffer_load_b32(rks, vo_ks[t], j * ks2 * (kD / 8), 0);
-                r.kr[t] = __builtin_amdgcn_raw_buffer_load_b16(rkr, vo_kr[t], j * ks2 * 2, 0);
-            }
-        }
-        buf_block<VB>(rv, vo_v0, sv, r.vw[0]);
-        buf_block<VB>(rv, vo_v1, sv, r.vw[1]);
+        for (int h2 = 0; h2 < 2; ++h2) buf_dwords<2 * VB>(rv, vo_v[h2], j * vs2 * kVcb, r.vw[h2]);
         r.nk = __builtin_amdgcn_raw_buffer_load_b16(rkn, vo_kn, j * ks2 * 2, 0);
         r.nv = __builtin_amdgcn_raw_buffer_load_b16(rvn, vo_vn, j * vs2 * 2, 0);
+        if constexpr (QJL) {
+            buf_dwords<4>(rks, vo_ks, j * ks2 * (kD / 8), r.ks);
+            r.kr = __builtin_amdgcn_raw_buffer_load_b16(rkr, vo_kn, j * ks2 * 2, 0);
+        }
     };
 
-    // transposed-read addresses (fixed per lane)
-    const int tr_row = 8 * lgrp + (lrow >> 2);
-    const int tr_half = 4 * (lrow & 3);
-    const int p_off0 = tr_row * kPRow + tr_half * 2;
-    const int p_off1 = p_off0 + 4 * kPRow;
-    const int v_off0 = vrow_off(tr_row) + tr_half * 2;
-    const int v_off1 = vrow_off(tr_row + 4) + tr_half * 2;
+    // transposed-read addresses (fixed per lane): lane j of each 16-lane group
+    // points at row j/4 of a 4-row band, column group j%4
+    const int band_row = (lane & 15) >> 2;
+    const int p_off = band_row * 8;
+    const int v_off = band_row * kVRow + (4 * (4 * (lane >> 4) + (lane & 3))) * 2;
 
     auto process = [&](int64_t j0, const regs & r) {
-        // ---------------- logits for tokens j0 .. j0+31 (two 16-token tiles)
-        floatx4 st[2];
+        // ---------------- logits: lane l <- 4 heads of token j0 + l
+        floatx4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int bl = 0; bl < 4; ++bl) {
             uint32_t bq[16];
-            unpack_block<KB>(klut, r.kw[t], bq);
-            floatx4 s = {0.f, 0.f, 0.f, 0.f};
+            unpack_block<KB>(klut, r.kw + KB * bl, bq);
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-                s = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[mi], as_half8(bq + 4 * mi), s, 0, 0, 0);
-            if constexpr (QJL) {
-                uint32_t bs[16];
-                unpack_signs(r.ks[t], bs);
-                floatx4 sq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-                    sq = __builtin_amdgcn_mfma_f32_16x16x32_f16(au[mi], as_half8(bs + 4 * mi), sq, 0, 0, 0);
-                const float gam = half_bits_to_float(r.kr[t]) * qjl_gain;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) s[q] = fmaf(gam, sq[q], s[q]);
+            for (int kk = 0; kk < 8; ++kk) {
+                const int gs = 8 * bl + kk;
+                const half4 bk = as_half4(bq[2 * kk], bq[2 * kk + 1]);
+                S = mfma4_bcast(gs & 15, aq[gs >> 4][0], bk, S);
+                S = mfma4_bcast(gs & 15, aq[gs >> 4][1], bk, S);
             }
-            // hi rows (lanes 0-15) + lo rows (lanes 16-31)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) s[q] += lane_xor<16>(s[q]);
-            st[t] = s;
         }
-        // lane l < 32 owns token j0 + l: tile l/16, column l%16
-        const bool own = lane < 32 && j0 + lane < w_end;
+        if constexpr (QJL) {
+            floatx4 Sq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int bl = 0; bl < 4; ++bl) {
+                uint32_t bs[16];
+                unpack_signs(r.ks[bl], bs);
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    const int gs = 8 * bl + kk;
+                    const half4 bk = as_half4(bs[2 * kk], bs[2 * kk + 1]);
+                    Sq = mfma4_bcast(gs & 15, au[gs >> 4][0], bk, Sq);
+                    Sq = mfma4_bcast(gs & 15, au[gs >> 4][1], bk, Sq);
+                }
+            }
+            const float gam = half_bits_to_float(r.kr) * qjl_gain;
+#pragma unroll
+            for (int h = 0; h < kG; ++h) S[h] = fmaf(gam, Sq[h], S[h]);
+        }
+        // ---------------- online softmax over the wave's tokens
+        const bool own = j0 + lane < w_end;
         const float ks_tok = own ? half_bits_to_float(r.nk) * kscale : 0.f;
         const float nv = half_bits_to_float(r.nv) * inv_sqrt_d;
-        const float lam = __logf(fmaxf(nv, 1e-26f));
-        float s[kG];
+        float s[kG], p[kG];
         bool over = false;
 #pragma unroll
         for (int h = 0; h < kG; ++h) {
-            const float v = (lane & 16) ? st[1][h] : st[0][h];
-            s[h] = own ? v * ks_tok : -INFINITY;
-            over |= s[h] + lam > mref[h] + kSlack;
+            s[h] = own ? S[h] * ks_tok : -INFINITY;
+            p[h] = __expf(s[h] - mref[h]);
+            over |= !(p[h] * nv <= w_cap);  // also catches inf * 0 before the first max
         }
         if (__any(over)) {
+            const float lam = __logf(fmaxf(nv, 1e-26f));
 #pragma unroll
             for (int h = 0; h < kG; ++h) {
                 const float mn = fmaxf(mref[h], wave_max(s[h] + lam));
                 const float alpha = mref[h] == -INFINITY ? 0.f : __expf(mref[h] - mn);
                 mref[h] = mn;
                 lsum[h] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt) acc[dt][h] *= alpha;
+                acc[0][h] *= alpha;
+                acc[1][h] *= alpha;
+                p[h] = __expf(s[h] - mn);
             }
         }
-        uint32_t wp[2];
 #pragma unroll
-        for (int h = 0; h < kG; h += 2) {
-            const float p0 = __expf(s[h] - mref[h]);
-            const float p1 = __expf(s[h + 1] - mref[h + 1]);
-            lsum[h] += p0;
-            lsum[h + 1] += p1;
-            wp[h / 2] = uint32_t(f16_bits(p0 * nv)) | (uint32_t(f16_bits(p1 * nv)) << 16);
-        }
-        if (lane < 32) *reinterpret_cast<u32x2 *>(ptile + lane * kPRow) = u32x2{wp[0], wp[1]};
+        for (int h = 0; h < kG; ++h) lsum[h] += p[h];
+        *reinterpret_cast<u32x2 *>(ptile + lane * 8) =
+            u32x2{uint32_t(f16_bits(p[0] * nv)) | (uint32_t(f16_bits(p[1] * nv)) << 16),
+                  uint32_t(f16_bits(p[2] * nv)) | (uint32_t(f16_bits(p[3] * nv)) << 16)};
 
-        // ---------------- values: dequantise 32 tokens x 4 blocks into LDS
+        // ---------------- values, 32 tokens per pass through the LDS tile
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int blk = (lane >> 5) + 2 * u;
-            uint32_t o[16];
-            unpack_block<VB>(vlut, r.vw[u], o);
-            uint8_t * dst = vtile + vrow_off(lane & 31) + blk * 64;
+        for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                *reinterpret_cast<u32x4 *>(dst + c * 16) = u32x4{o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]};
-        }
-        // ---------------- O[h, :] += W[h, 32 tokens] . V[32 tokens, :]
-        const half8 aw = tr_read(ptile, p_off0, p_off1);
+            for (int u = 0; u < 2; ++u) {
+                const int blk = 2 * (lane >> 5) + u;
+                uint32_t o[16];
+                unpack_block<VB>(vlut, r.vw[h2] + VB * u, o);
+                uint8_t * dst = vtile + vrow_off(lane & 31) + blk * 64;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            const half8 bv = tr_read(vtile, v_off0 + 32 * dt, v_off1 + 32 * dt);
-            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, bv, acc[dt], 0, 0, 0);
+                for (int c = 0; c < 4; ++c)
+                    *reinterpret_cast<u32x4 *>(dst + c * 16) = u32x4{o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]};
+            }
+#pragma unroll
+            for (int kk = 0; kk < kHalf / 4; ++kk) {
+                const half4 aw = tr_read4(ptile, (kHalf * h2 + 4 * kk) * 8 + p_off);
+                // band rows 4kk..4kk+3: bit 2 of the row is kk & 1
+                const int band = 4 * kk * kVRow + (kk & 1) * 16;
+#pragma unroll
+                for (int dh = 0; dh < 2; ++dh) {
+                    const half4 bv = tr_read4(vtile, v_off + band + 128 * dh);
+                    acc[dh] = __builtin_amdgcn_mfma_f32_4x4x4f16(aw, bv, acc[dh], 0, 0, 0);
+                }
+            }
         }
     };
 
-    regs cur, nxt;
-    if (w_begin < w_end) load_step(w_begin, cur);
-    for (int64_t j0 = w_begin; j0 < w_end; j0 += kStep) {
-        if (j0 + kStep < w_end) load_step(j0 + kStep, nxt);
-        process(j0, cur);
-        cur = nxt;
+    // Ping-pong register sets: step i+1 loads into the set step i is not using.
+    // Loads are issued unconditionally (past the valid range a buffer load
+    // reads zeros or ignored positions) so that the wait counts stay static.
+    regs r0, r1;
+    load_step(w_begin, r0);
+    for (int64_t j0 = w_begin; j0 < w_end; j0 += 2 * kStep) {
+        load_step(j0 + kStep, r1);
+        process(j0, r0);
+        if (j0 + kStep >= w_end) break;
+        load_step(j0 + 2 * kStep, r0);
+        process(j0 + kStep, r1);
     }
 
-    // ---- wave results: m, l (summed over the 32 token lanes), acc rows 0..3
+    // ---- wave results: m, l (summed over the token lanes), acc
 #pragma unroll
     for (int h = 0; h < kG; ++h) lsum[h] = wave_sum(lsum[h]);
     __syncthreads();
     float * res = reinterpret_cast<float *>(lds + wave * kWaveLds);  // [kG][kD + 2]
-    if (lane < 16) {
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            const int c = 16 * dt + lrow;  // V tile column -> rotated-domain dim
-            const int dim = 32 * (c >> 5) + block_code_of_pos<VB>(c & 31);
+    for (int dh = 0; dh < 2; ++dh) {
+        const int c = 64 * dh + 4 * (lane >> 2) + (lane & 3);  // V tile column -> rotated-domain dim
+        const int dim = 32 * (c >> 5) + block_code_of_pos<VB>(c & 31);
 #pragma unroll
-            for (int h = 0; h < kG; ++h) res[h * (kD + 2) + 2 + dim] = acc[dt][h];
-        }
+        for (int h = 0; h < kG; ++h) res[h * (kD + 2) + 2 + dim] = acc[dh][h];
     }
     if (lane < kG) {
         res[lane * (kD + 2)] = mref[lane];
@@ -404,6 +433,8 @@ int attend_mfma_blocks_per_cu(const dev_tables & kt, const dev_tables & vt) {
     }
     return 1;
 }
+
+int attend_mfma_chunk_quantum() { return 4 * kStep; }
 
 bool attend_mfma_shape_ok(const dev_tables & kt, const dev_tables & vt, int32_t Hq, int32_t Hkv) {
     return kt.d == kD && vt.d == kD && Hq == kG * Hkv && (!kt.qjl || kt.m == kD);
