@@ -41,14 +41,16 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;
 constexpr int kG = 4;
 constexpr int kStep = 64;                  // tokens per wave iteration (one per lane)
-constexpr int kHalf = 32;                  // tokens per V tile pass
+constexpr int kPass = 16;                  // tokens per V tile pass
+constexpr int kPasses = kStep / kPass;
 constexpr int kVRow = 2 * kD + 32;         // bytes per token row of the V tile (padded)
-constexpr int kVTile = kHalf * kVRow;      // 9216 B
+constexpr int kVTile = kPass * kVRow;      // 4608 B
 constexpr int kPTile = kStep * 8;          // 64 tokens x 4 heads x fp16
 constexpr int kWaveLds = kVTile + kPTile;
 constexpr float kSlack = 4.0f;
@@ -107,7 +109,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void * base, u
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), kRsrcWord3);
 }
 
-// N consecutive dwords at byte offset voff + soff (N even).
+// N consecutive dwords at byte offset voff + soff.
 template <int N>
 __device__ __forceinline__ void buf_dwords(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t * w) {
     int k = 0;
@@ -119,17 +121,49 @@ __device__ __forceinline__ void buf_dwords(__amdgpu_buffer_rsrc_t r, uint32_t vo
         w[k + 2] = v.z;
         w[k + 3] = v.w;
     }
-    if constexpr (N % 4 == 2) {
+    if constexpr (N % 4 == 3) {
+        const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, voff + 4 * (N - 3), soff, 0);
+        w[N - 3] = v.x;
+        w[N - 2] = v.y;
+        w[N - 1] = v.z;
+    } else if constexpr (N % 4 == 2) {
         const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff + 4 * (N - 2), soff, 0);
         w[N - 2] = v.x;
         w[N - 1] = v.y;
+    } else if constexpr (N % 4 == 1) {
+        w[N - 1] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 4 * (N - 1), soff, 0);
     }
+}
+
+// 3-bit keys are decoded through a 64-entry LDS table indexed by two
+// consecutive codes (6 bits of the row's bit stream): entry e holds the fp16
+// centroids of codes e & 7 and e >> 3.  The table is stored 32 times, copy c
+// in bank c (entry e of copy c at byte 128 e + 4 c), and lane l reads copy
+// l % 32, so the 32 lanes served together never share a bank whatever codes
+// they hold.  A lookup costs a shift, a mask-or and one ds_read_b32 per two
+// codes.
+template <int KB>
+constexpr bool pair_table() { return KB == 3; }
+constexpr int kPairCopies = 32;
+
+// LDS byte offset of pair p (codes 2p, 2p+1) of the code row held in w, in
+// the copy whose offset is lane_off.
+__device__ __forceinline__ uint32_t pair_offset(const uint32_t * w, int p, uint32_t lane_off) {
+    const int s = 6 * p, wi = s >> 5, o = s & 31;
+    uint32_t t;
+    if (o > 26)
+        t = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], o - 7);
+    else if (o >= 7)
+        t = w[wi] >> (o - 7);
+    else
+        t = w[wi] << (7 - o);
+    return (t & (63u << 7)) | lane_off;
 }
 
 template <int KB, int VB, bool QJL>
 struct step_regs {
     uint32_t kw[4 * KB];     // K code row of token lane (4 blocks)
-    uint32_t vw[2][2 * VB];  // V blocks 2(lane>>5), 2(lane>>5)+1 of tokens (lane&31), 32+(lane&31)
+    uint32_t vw[kPasses][VB];  // V block (lane>>4) of token 16 pass + (lane&15)
     uint32_t ks[QJL ? 4 : 1];
     uint16_t kr;             // QJL residual norm
     uint16_t nk, nv;         // K and V norms of token lane
@@ -147,7 +181,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 256), amdgpu_waves_per_
 void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
                                                           const attend_args a) {
     constexpr uint32_t kKcb = kD * KB / 8, kVcb = kD * VB / 8;
-    __shared__ __align__(16) uint8_t lds[4 * kWaveLds];
+    // one LDS array: the pair table (if any) at offset 0, so that its lookups
+    // need no base add, then the four waves' tiles
+    constexpr int kTabBytes = pair_table<KB>() ? 64 * kPairCopies * 4 : 0;
+    __shared__ __align__(16) uint8_t lds_all[kTabBytes + 4 * kWaveLds];
+    uint32_t * const ktab = reinterpret_cast<uint32_t *>(lds_all);
+    uint8_t * const lds = lds_all + kTabBytes;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int lane = tid & 63;
@@ -174,7 +213,8 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
             const int bl = gs >> 3, kk = gs & 7;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float x = qrow[32 * bl + block_code_of_pos<KB>(4 * kk + i)];
+                const int kpos = pair_table<KB>() ? 4 * kk + i : block_code_of_pos<KB>(4 * kk + i);
+                const float x = qrow[32 * bl + kpos];
                 const _Float16 hi = static_cast<_Float16>(x);
                 aq[set][0][i] = hi;
                 aq[set][1][i] = static_cast<_Float16>(x - static_cast<float>(hi));
@@ -186,6 +226,13 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
                 }
             }
         }
+    }
+    if constexpr (pair_table<KB>()) {
+        for (int i = tid; i < 64 * kPairCopies; i += 256) {
+            const int e = i / kPairCopies;
+            ktab[i] = uint32_t(f16_bits(kt.cb[e & 7])) | (uint32_t(f16_bits(kt.cb[e >> 3])) << 16);
+        }
+        __syncthreads();
     }
     const lut16 klut = make_lut(kt.cb);
     const lut16 vlut = make_lut(vt.cb);
@@ -222,17 +269,17 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     const uint32_t vo_kn = uint32_t(lane) * ks2 * 2;
     const uint32_t vo_ks = uint32_t(lane) * ks2 * (kD / 8);
     const uint32_t vo_vn = uint32_t(lane) * vs2 * 2;
-    uint32_t vo_v[2];
+    uint32_t vo_v[kPasses];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-        vo_v[h2] = uint32_t(kHalf * h2 + (lane & 31)) * vs2 * kVcb + (lane >> 5) * 8 * VB;
+    for (int hp = 0; hp < kPasses; ++hp)
+        vo_v[hp] = uint32_t(kPass * hp + (lane & 15)) * vs2 * kVcb + (lane >> 4) * 4 * VB;
 
     using regs = step_regs<KB, VB, QJL>;
     auto load_step = [&](int64_t j0, regs & r) {
         const uint32_t j = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(j0));  // wave-uniform
         buf_dwords<4 * KB>(rk, vo_k, j * ks2 * kKcb, r.kw);
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) buf_dwords<2 * VB>(rv, vo_v[h2], j * vs2 * kVcb, r.vw[h2]);
+        for (int hp = 0; hp < kPasses; ++hp) buf_dwords<VB>(rv, vo_v[hp], j * vs2 * kVcb, r.vw[hp]);
         r.nk = __builtin_amdgcn_raw_buffer_load_b16(rkn, vo_kn, j * ks2 * 2, 0);
         r.nv = __builtin_amdgcn_raw_buffer_load_b16(rvn, vo_vn, j * vs2 * 2, 0);
         if constexpr (QJL) {
@@ -250,16 +297,29 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     auto process = [&](int64_t j0, const regs & r) {
         // ---------------- logits: lane l <- 4 heads of token j0 + l
         floatx4 S = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (pair_table<KB>()) {
+            const uint8_t * tab = reinterpret_cast<const uint8_t *>(ktab);
+            const uint32_t lane_off = uint32_t(lane & 31) * 4;
 #pragma unroll
-        for (int bl = 0; bl < 4; ++bl) {
-            uint32_t bq[16];
-            unpack_block<KB>(klut, r.kw + KB * bl, bq);
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const int gs = 8 * bl + kk;
-                const half4 bk = as_half4(bq[2 * kk], bq[2 * kk + 1]);
+            for (int gs = 0; gs < 32; ++gs) {
+                const uint32_t lo = *reinterpret_cast<const uint32_t *>(tab + pair_offset(r.kw, 2 * gs, lane_off));
+                const uint32_t hi = *reinterpret_cast<const uint32_t *>(tab + pair_offset(r.kw, 2 * gs + 1, lane_off));
+                const half4 bk = as_half4(lo, hi);
                 S = mfma4_bcast(gs & 15, aq[gs >> 4][0], bk, S);
                 S = mfma4_bcast(gs & 15, aq[gs >> 4][1], bk, S);
+            }
+        } else {
+#pragma unroll
+            for (int bl = 0; bl < 4; ++bl) {
+                uint32_t bq[16];
+                unpack_block<KB>(klut, r.kw + KB * bl, bq);
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    const int gs = 8 * bl + kk;
+                    const half4 bk = as_half4(bq[2 * kk], bq[2 * kk + 1]);
+                    S = mfma4_bcast(gs & 15, aq[gs >> 4][0], bk, S);
+                    S = mfma4_bcast(gs & 15, aq[gs >> 4][1], bk, S);
+                }
             }
         }
         if constexpr (QJL) {
@@ -311,22 +371,20 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
             u32x2{uint32_t(f16_bits(p[0] * nv)) | (uint32_t(f16_bits(p[1] * nv)) << 16),
                   uint32_t(f16_bits(p[2] * nv)) | (uint32_t(f16_bits(p[3] * nv)) << 16)};
 
-        // ---------------- values, 32 tokens per pass through the LDS tile
+        // ---------------- values, 16 tokens per pass through the LDS tile
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int blk = 2 * (lane >> 5) + u;
+        for (int hp = 0; hp < kPasses; ++hp) {
+            {
                 uint32_t o[16];
-                unpack_block<VB>(vlut, r.vw[h2] + VB * u, o);
-                uint8_t * dst = vtile + vrow_off(lane & 31) + blk * 64;
+                unpack_block<VB>(vlut, r.vw[hp], o);
+                uint8_t * dst = vtile + vrow_off(lane & 15) + (lane >> 4) * 64;
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
                     *reinterpret_cast<u32x4 *>(dst + c * 16) = u32x4{o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]};
             }
 #pragma unroll
-            for (int kk = 0; kk < kHalf / 4; ++kk) {
-                const half4 aw = tr_read4(ptile, (kHalf * h2 + 4 * kk) * 8 + p_off);
+            for (int kk = 0; kk < kPass / 4; ++kk) {
+                const half4 aw = tr_read4(ptile, (kPass * hp + 4 * kk) * 8 + p_off);
                 // band rows 4kk..4kk+3: bit 2 of the row is kk & 1
                 const int band = 4 * kk * kVRow + (kk & 1) * 16;
 #pragma unroll
