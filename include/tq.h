@@ -130,10 +130,13 @@ int64_t tq_sign_bytes(const struct tq_config * cfg);
  * x: device pointer, dtype TQ_DTYPE_F32 or TQ_DTYPE_BF16; element (i0,i1,i2,k)
  * at x[i0*x_stride[0] + i1*x_stride[1] + i2*x_stride[2] + k] (strides in
  * elements; the d elements of a vector are contiguous and 16-byte aligned).
- * out: planes to write (caller-owned device memory).  n0*n1*n2 == 0 is a no-op.
- * The rotation and z are evaluated in double precision, so codes and fp16
- * norms match a float64 evaluation of the same rule except within rounding
- * distance (~1e-15 relative) of a threshold or of an fp16 rounding midpoint.
+ * out: planes to write (caller-owned device memory).  n0*n1*n2 == 0 is a no-op;
+ * more than 2^32 - 1 vectors in one call gives TQ_STATUS_UNSUPPORTED.
+ * Precision: the norm is accumulated in double, so fp16 norms match a float64
+ * evaluation except within ~1e-15 relative of an fp16 rounding midpoint.  For
+ * an MSE-only ctx the rotation runs in fp32: a code can differ from a float64
+ * evaluation only within ~1e-6 of a threshold.  For a qjl ctx the rotation,
+ * residual and gamma run in double as well.
  */
 int32_t tq_encode(const struct tq_ctx * ctx, const void * x, int32_t x_dtype,
                   int64_t n0, int64_t n1, int64_t n2, const int64_t x_stride[3],

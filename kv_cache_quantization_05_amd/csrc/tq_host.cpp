@@ -168,6 +168,8 @@ int32_t tq_encode(const tq_ctx * ctx, const void * x, int32_t x_dtype, int64_t n
     if (const char * why = check_planes(ctx, out, ctx->cfg.qjl != 0))
         return fail(TQ_STATUS_INVALID_ARG, "%s", why);
     tq::encode_args a{x, x_dtype, n0, n1, n2, x_stride[0], x_stride[1], x_stride[2], out};
+    if (!tq::encode_grid_supported(a))
+        return fail(TQ_STATUS_UNSUPPORTED, "encode grids are limited to 2^32 - 1 vectors per call");
     return device_status(tq::launch_encode(ctx->tab, a, static_cast<hipStream_t>(hip_stream)),
                          "encode launch");
 }

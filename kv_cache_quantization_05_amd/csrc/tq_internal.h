@@ -39,6 +39,7 @@ struct encode_args {
     tq_planes out;
 };
 hipError_t launch_encode(const dev_tables & t, const encode_args & a, hipStream_t s);
+bool encode_grid_supported(const encode_args & a);  // n0*n1*n2 < 2^32
 
 // Query preparation: qp[i] = [ R q_i (d floats) | S R q_i (m floats, qjl) ].
 hipError_t launch_query_prep(const dev_tables & t, const float * q, int64_t n, float * qp,
