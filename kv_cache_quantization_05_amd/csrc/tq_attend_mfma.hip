@@ -203,52 +203,6 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     // ---- query operands.  K-step gs (0..31) covers dims of block gs/8 at
     // positions 4(gs%8)..+3; its query comes from block gs%16, i.e. lanes
     // 4(gs%16)..+3 (row = head).  This lane sources k-steps lane/4 and lane/4+16.
-    half4 aq[2][2], au[2][2];
-    {
-        const int h = lane & 3;
-        const float * qrow = a.qp + (int64_t(b) * a.Hq + g * kG + h) * a.qp_stride;
-#pragma unroll
-        for (int set = 0; set < 2; ++set) {
-            const int gs = (lane >> 2) + 16 * set;
-            const int bl = gs >> 3, kk = gs & 7;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int kpos = pair_table<KB>() ? 4 * kk + i : block_code_of_pos<KB>(4 * kk + i);
-                const float x = qrow[32 * bl + kpos];
-                const _Float16 hi = static_cast<_Float16>(x);
-                aq[set][0][i] = hi;
-                aq[set][1][i] = static_cast<_Float16>(x - static_cast<float>(hi));
-                if constexpr (QJL) {
-                    const float u = qrow[kD + 32 * bl + sign_bit_of_pos(4 * kk + i)];
-                    const _Float16 uh = static_cast<_Float16>(u);
-                    au[set][0][i] = uh;
-                    au[set][1][i] = static_cast<_Float16>(u - static_cast<float>(uh));
-                }
-            }
-        }
-    }
-    if constexpr (pair_table<KB>()) {
-        for (int i = tid; i < 64 * kPairCopies; i += 256) {
-            const int e = i / kPairCopies;
-            ktab[i] = uint32_t(f16_bits(kt.cb[e & 7])) | (uint32_t(f16_bits(kt.cb[e >> 3])) << 16);
-        }
-        __syncthreads();
-    }
-    const lut16 klut = make_lut(kt.cb);
-    const lut16 vlut = make_lut(vt.cb);
-    const float inv_sqrt_d = 1.0f / sqrtf(float(kD));
-    const float kscale = a.scale * inv_sqrt_d;
-    const float qjl_gain = sqrtf(0.5f * float(M_PI)) / float(kD) * sqrtf(float(kD));
-    const float w_cap = __expf(kSlack);
-
-    floatx4 acc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-    float mref[kG], lsum[kG];
-#pragma unroll
-    for (int h = 0; h < kG; ++h) {
-        mref[h] = -INFINITY;
-        lsum[h] = 0.f;
-    }
-
     // ---- buffer resources over this (batch, KV head)'s valid positions
     const uint32_t ks2 = static_cast<uint32_t>(a.k.stride[2]);
     const uint32_t vs2 = static_cast<uint32_t>(a.v.stride[2]);
@@ -287,6 +241,116 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
             r.kr = __builtin_amdgcn_raw_buffer_load_b16(rkr, vo_kn, j * ks2 * 2, 0);
         }
     };
+
+    // the first step's codes are in flight while the queries and tables are set up
+    regs r0, r1;
+    load_step(w_begin, r0);
+
+    if constexpr (pair_table<KB>()) {
+        for (int i = tid; i < 64 * kPairCopies; i += 256) {
+            const int e = i / kPairCopies;
+            ktab[i] = uint32_t(f16_bits(kt.cb[e & 7])) | (uint32_t(f16_bits(kt.cb[e >> 3])) << 16);
+        }
+    }
+
+    // ---- rotated queries.  MSE-only keys: each wave rotates its 4 heads
+    // itself (q' = D1 H D2 q / sqrt(d), [TQ+ guide] §5.3): lane l holds
+    // coordinates 8(l%16)..+7 of head l/16; three butterfly stages run in
+    // registers, four across the 16 lanes of the head; q' is staged in the
+    // wave's (not yet used) V tile.  QJL keys read q' and S q' prepared by the
+    // query kernel.
+    const float * qsrc;
+    int64_t qstride;
+    if constexpr (!QJL) {
+        const int h = lane >> 4, e0 = 8 * (lane & 15);
+        const float4 * src = reinterpret_cast<const float4 *>(a.q + (int64_t(b) * a.Hq + g * kG + h) * kD + e0);
+        const float4 u0 = src[0], u1 = src[1];
+        float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        const uint32_t s2 = kt.d2[e0 >> 5] >> (e0 & 31), s1 = kt.d1[e0 >> 5] >> (e0 & 31);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if ((s2 >> i) & 1) v[i] = -v[i];
+#pragma unroll
+        for (int hh = 1; hh < 8; hh <<= 1)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if ((i & hh) == 0) {
+                    const float x0 = v[i], x1 = v[i + hh];
+                    v[i] = x0 + x1;
+                    v[i + hh] = x0 - x1;
+                }
+        {
+            const float sg = (lane & 1) ? -1.f : 1.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(sg, v[i], lane_xor<1>(v[i]));
+        }
+        {
+            const float sg = (lane & 2) ? -1.f : 1.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(sg, v[i], lane_xor<2>(v[i]));
+        }
+        {
+            const float sg = (lane & 4) ? -1.f : 1.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(sg, v[i], lane_xor<4>(v[i]));
+        }
+        {
+            const float sg = (lane & 8) ? -1.f : 1.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(sg, v[i], lane_xor<8>(v[i]));
+        }
+        const float rs = 1.0f / sqrtf(float(kD));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = ((s1 >> i) & 1) ? -v[i] * rs : v[i] * rs;
+        float4 * dst = reinterpret_cast<float4 *>(vtile + (h * kD + e0) * 4);
+        dst[0] = float4{v[0], v[1], v[2], v[3]};
+        dst[1] = float4{v[4], v[5], v[6], v[7]};
+        qsrc = reinterpret_cast<const float *>(vtile);
+        qstride = kD;
+    } else {
+        qsrc = a.qp + (int64_t(b) * a.Hq + g * kG) * a.qp_stride;
+        qstride = a.qp_stride;
+    }
+    __syncthreads();  // q' staged (and the pair table, below, filled)
+
+    half4 aq[2][2], au[2][2];
+    {
+        const int h = lane & 3;
+        const float * qrow = qsrc + h * qstride;
+#pragma unroll
+        for (int set = 0; set < 2; ++set) {
+            const int gs = (lane >> 2) + 16 * set;
+            const int bl = gs >> 3, kk = gs & 7;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int kpos = pair_table<KB>() ? 4 * kk + i : block_code_of_pos<KB>(4 * kk + i);
+                const float x = qrow[32 * bl + kpos];
+                const _Float16 hi = static_cast<_Float16>(x);
+                aq[set][0][i] = hi;
+                aq[set][1][i] = static_cast<_Float16>(x - static_cast<float>(hi));
+                if constexpr (QJL) {
+                    const float u = qrow[kD + 32 * bl + sign_bit_of_pos(4 * kk + i)];
+                    const _Float16 uh = static_cast<_Float16>(u);
+                    au[set][0][i] = uh;
+                    au[set][1][i] = static_cast<_Float16>(u - static_cast<float>(uh));
+                }
+            }
+        }
+    }
+    const lut16 klut = make_lut(kt.cb);
+    const lut16 vlut = make_lut(vt.cb);
+    const float inv_sqrt_d = 1.0f / sqrtf(float(kD));
+    const float kscale = a.scale * inv_sqrt_d;
+    const float qjl_gain = sqrtf(0.5f * float(M_PI)) / float(kD) * sqrtf(float(kD));
+    const float w_cap = __expf(kSlack);
+
+    floatx4 acc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+    float mref[kG], lsum[kG];
+#pragma unroll
+    for (int h = 0; h < kG; ++h) {
+        mref[h] = -INFINITY;
+        lsum[h] = 0.f;
+    }
 
     // transposed-read addresses (fixed per lane): lane j of each 16-lane group
     // points at row j/4 of a 4-row band, column group j%4
@@ -399,8 +463,6 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     // Ping-pong register sets: step i+1 loads into the set step i is not using.
     // Loads are issued unconditionally (past the valid range a buffer load
     // reads zeros or ignored positions) so that the wait counts stay static.
-    regs r0, r1;
-    load_step(w_begin, r0);
     for (int64_t j0 = w_begin; j0 < w_end; j0 += 2 * kStep) {
         load_step(j0 + kStep, r1);
         process(j0, r0);

@@ -231,61 +231,63 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(const dev_tables kt
 }
 
 // Log-sum-exp merge of the per-chunk states of one (batch, query head), then
-// the inverse rotation o = R^T o' back to the original domain.
+// the inverse rotation o = R^T o' back to the original domain.  Two passes:
+// the block's 256 threads find the largest chunk maximum M, then wave w
+// accumulates chunks w, w+4, ... weighted by exp(m_c - M) (lane = dims
+// lane, lane+64, ...), with several chunks' loads in flight, and the four
+// waves' sums are added through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void attend_merge_kernel(const dev_tables vt, const attend_args a) {
-    constexpr int PARTS = 256 / D;
-    __shared__ float red[256];
-    __shared__ float part_acc[PARTS][D];
+    constexpr int PER = D >= 64 ? D / 64 : 1;
+    __shared__ float red[4];
+    __shared__ float part_acc[4][D];
+    __shared__ float part_l[4];
     __shared__ float s[D];
     const int h = blockIdx.x, b = blockIdx.y;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const float * base = a.partial + (int64_t(b) * a.Hq + h) * a.n_chunks * (D + 2);
     const int n = a.n_chunks;
     float m = -INFINITY;
     for (int c = tid; c < n; c += 256) m = fmaxf(m, base[int64_t(c) * (D + 2)]);
-    red[tid] = m;
+    m = wave_max(m);
+    if (lane == 0) red[wave] = m;
     __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-        __syncthreads();
-    }
-    const float M = red[0];
-    __syncthreads();
-    float l = 0.f;
-    if (M != -INFINITY)
-        for (int c = tid; c < n; c += 256) {
-            const float * p = base + int64_t(c) * (D + 2);
-            l = fmaf(p[1], __expf(p[0] - M), l);
-        }
-    red[tid] = l;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if (tid < o) red[tid] += red[tid + o];
-        __syncthreads();
-    }
-    const float Lsum = red[0];
-    const int e = tid % D, part = tid / D;
-    float acc0 = 0.f, acc1 = 0.f;
-    if (M != -INFINITY) {
-        int c = part;
-        for (; c + PARTS < n; c += 2 * PARTS) {
-            const float * p0 = base + int64_t(c) * (D + 2);
-            const float * p1 = p0 + int64_t(PARTS) * (D + 2);
-            acc0 = fmaf(p0[2 + e], __expf(p0[0] - M), acc0);
-            acc1 = fmaf(p1[2 + e], __expf(p1[0] - M), acc1);
-        }
-        if (c < n) {
-            const float * p0 = base + int64_t(c) * (D + 2);
-            acc0 = fmaf(p0[2 + e], __expf(p0[0] - M), acc0);
-        }
-    }
-    part_acc[part][e] = acc0 + acc1;
-    __syncthreads();
-    if (tid < D) {
-        float o = 0.f;
+    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float acc[PER], l = 0.f;
 #pragma unroll
-        for (int p = 0; p < PARTS; ++p) o += part_acc[p][tid];
+    for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+    if (M != -INFINITY) {
+        constexpr int U = 8;  // chunks per batch of loads
+        for (int c0 = wave; c0 < n; c0 += 4 * U) {
+            float mc[U], lc[U], vc[U][PER];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + 4 * u;
+                const float * p = base + int64_t(c < n ? c : c0) * (D + 2);
+                mc[u] = c < n ? p[0] : -INFINITY;
+                lc[u] = p[1];
+#pragma unroll
+                for (int i = 0; i < PER; ++i) vc[u][i] = (lane + 64 * i < D) ? p[2 + lane + 64 * i] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float w = mc[u] == -INFINITY ? 0.f : __expf(mc[u] - M);
+                l = fmaf(w, lc[u], l);
+#pragma unroll
+                for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, vc[u][i], acc[i]);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+        if (lane + 64 * i < D) part_acc[wave][lane + 64 * i] = acc[i];
+    if (lane == 0) part_l[wave] = l;
+    __syncthreads();
+    const float Lsum = part_l[0] + part_l[1] + part_l[2] + part_l[3];
+    if (tid < D) {
+        const float o0 = part_acc[0][tid] + part_acc[1][tid] + part_acc[2][tid] + part_acc[3][tid];
+        float o = o0;
         o = (M != -INFINITY && Lsum > 0.f) ? o / Lsum : 0.f;
         // o_orig = R^T o = D2 . H . D1 . o / sqrt(d)
         if ((vt.d1[tid >> 5] >> (tid & 31)) & 1) o = -o;
@@ -312,7 +314,13 @@ template <int D, int KB, int VB, bool QJL>
 hipError_t launch_attend_g(const dev_tables & kt, const dev_tables & vt, const attend_args & a,
                            hipStream_t s) {
     const dim3 grid(a.n_chunks, a.Hkv, a.B);
-    if (attend_mfma_supported(kt, vt, a)) {
+    const bool mfma = attend_mfma_supported(kt, vt, a);
+    // the matrix-core kernel rotates MSE-only queries itself
+    if (!mfma || kt.qjl) {
+        hipError_t e = launch_query_prep(kt, a.q, int64_t(a.B) * a.Hq, a.qp, a.qp_stride, s);
+        if (e != hipSuccess) return e;
+    }
+    if (mfma) {
         hipError_t e = launch_attend_mfma_partial(kt, vt, a, s);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((attend_merge_kernel<D>), dim3(a.Hq, a.B), dim3(256), 0, s, vt, a);

@@ -265,9 +265,8 @@ int32_t tq_attend_decode(const tq_ctx * k_ctx, const tq_ctx * v_ctx, const float
     const int64_t qp_stride = d + k_ctx->tab.m;
     char * ws = static_cast<char *>(workspace);
     float * qp = reinterpret_cast<float *>(ws);
-    hipError_t e = tq::launch_query_prep(k_ctx->tab, q, int64_t(B) * Hq, qp, qp_stride, s);
-    if (e != hipSuccess) return device_status(e, "query prep launch");
     tq::attend_args a{};
+    a.q = q;
     a.qp = qp;
     a.qp_stride = qp_stride;
     a.k = k;

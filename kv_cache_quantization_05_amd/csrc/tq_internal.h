@@ -46,7 +46,8 @@ hipError_t launch_query_prep(const dev_tables & t, const float * q, int64_t n, f
                              int64_t qp_stride, hipStream_t s);
 
 struct attend_args {
-    const float * qp;           // prepared queries [B*Hq, qp_stride]
+    const float * q;            // queries [B*Hq, d] as given
+    float * qp;                 // prepared queries [B*Hq, qp_stride] (workspace)
     int64_t qp_stride;
     tq_planes k, v;
     const int32_t * seq_lens;
