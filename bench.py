@@ -15,7 +15,6 @@ decodes copy i + R/2, written R/2 steps earlier.
 """
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -34,15 +33,6 @@ def packed_bytes_per_token_head(w, code_bytes_k, code_bytes_v, sign_bytes_k):
     return kb + code_bytes_v + 2
 
 
-def kernel_source_hash():
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "kv_cache_quantization_05_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
-    return h.hexdigest()[:16]
-
-
 def traffic_from_profiles(kernel, workload):
     """HBM bytes per launch measured by rocprofv3 counters, if recorded for the
     current kernel sources (profiles/traffic.json); otherwise None."""
@@ -54,6 +44,8 @@ def traffic_from_profiles(kernel, workload):
     except Exception:
         return None
     ent = rec.get(f"{workload}:{kernel}")
+    from kv_cache_quantization_05_amd.rocpd_summary import kernel_source_hash
+
     if not ent or ent.get("source_hash") != kernel_source_hash():
         return None
     return ent.get("bytes_per_launch")
@@ -200,8 +192,10 @@ def main():
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(kernel, w.name),
                 "algorithmic_bytes": int(alg_bytes), "avg_ms": round(ms, 5)}
 
+    # per launch: one tq_attend_decode call; one tq_encode call (the K and V
+    # launches of a step averaged, as rocprofv3 averages their dispatches)
     r_dec = roof("attend_decode", dec_gbs, packed, dec_avg)
-    r_enc = roof("encode", enc_gbs, enc_bytes, enc_avg)
+    r_enc = roof("encode", enc_gbs, enc_bytes / 2, enc_avg / 2)
     line = {
         "metric": "packed-KV decode-attention GB/s (% of HBM peak) + encode Mtok/s, 1 GPU",
         "value": round(dec_gbs, 2),

@@ -18,10 +18,12 @@
 // merge kernel rotates it back ([TQ+ guide] §6.1).
 //
 // Memory: each wave streams a contiguous token range with buffer loads whose
-// per-lane offsets are fixed and whose per-step offset is one scalar; the
-// resource's size is the (batch, head)'s valid length, so positions past it
+// per-lane offsets are fixed; each step's resources start at the step's first
+// token and end at the (batch, head)'s valid length, so positions past it
 // read as zero.  The next step's codes are loaded while the current one is
-// processed (ping-pong register sets, unconditional loads).
+// processed (ping-pong register sets; a load is issued for every step, and
+// one past the wave's range gets empty resources, so it costs no memory
+// traffic).
 //
 // Softmax bookkeeping per wave: a wave-uniform reference m per head, raised
 // only when a weight w = exp(s - m) * N_v/sqrt(d) would exceed e^kSlack (so
@@ -173,7 +175,7 @@ struct step_regs {
 // the loop still fits without spilling, else the compiler's choice.
 template <int KB, int VB, bool QJL>
 constexpr int waves_per_simd() {
-    return (KB + VB <= 6 && KB != 4 && VB != 4 && (!QJL || KB + VB == 4)) ? 4 : 1;
+    return (!QJL && VB == 3 && KB <= 3) ? 4 : 1;
 }
 
 template <int KB, int VB, bool QJL>
@@ -203,21 +205,23 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     // ---- query operands.  K-step gs (0..31) covers dims of block gs/8 at
     // positions 4(gs%8)..+3; its query comes from block gs%16, i.e. lanes
     // 4(gs%16)..+3 (row = head).  This lane sources k-steps lane/4 and lane/4+16.
-    // ---- buffer resources over this (batch, KV head)'s valid positions
+    // ---- per-step buffer resources.  A step's resources start at its first
+    // token and end at the (batch, head)'s valid length L, so a lane whose
+    // token is at or past L reads zeros: the range check of a raw buffer load
+    // covers the per-lane offset, not the scalar one, so the step position
+    // lives in the base address.  A step at or past the wave's end gets empty
+    // resources: its loads return zeros without touching memory, and the wait
+    // counts stay static.
     const uint32_t ks2 = static_cast<uint32_t>(a.k.stride[2]);
     const uint32_t vs2 = static_cast<uint32_t>(a.v.stride[2]);
-    const uint32_t Lu = static_cast<uint32_t>(L);
     const int64_t kvec = int64_t(b) * a.k.stride[0] + int64_t(g) * a.k.stride[1];
     const int64_t vvec = int64_t(b) * a.v.stride[0] + int64_t(g) * a.v.stride[1];
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k.codes + kvec * kKcb, Lu * ks2 * kKcb);
-    const __amdgpu_buffer_rsrc_t rkn = make_rsrc(a.k.norms + kvec, Lu * ks2 * 2);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v.codes + vvec * kVcb, Lu * vs2 * kVcb);
-    const __amdgpu_buffer_rsrc_t rvn = make_rsrc(a.v.norms + vvec, Lu * vs2 * 2);
-    __amdgpu_buffer_rsrc_t rks = rk, rkr = rk;
-    if constexpr (QJL) {
-        rks = make_rsrc(a.k.signs + kvec * (kD / 8), Lu * ks2 * (kD / 8));
-        rkr = make_rsrc(a.k.rnorms + kvec, Lu * ks2 * 2);
-    }
+    const uint8_t * const kc0 = a.k.codes + kvec * kKcb;
+    const uint16_t * const kn0 = a.k.norms + kvec;
+    const uint8_t * const vc0 = a.v.codes + vvec * kVcb;
+    const uint16_t * const vn0 = a.v.norms + vvec;
+    const uint8_t * const ks0 = QJL ? a.k.signs + kvec * (kD / 8) : nullptr;
+    const uint16_t * const kr0 = QJL ? a.k.rnorms + kvec : nullptr;
     // per-lane byte offsets relative to the step's first token
     const uint32_t vo_k = uint32_t(lane) * ks2 * kKcb;
     const uint32_t vo_kn = uint32_t(lane) * ks2 * 2;
@@ -230,15 +234,18 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
 
     using regs = step_regs<KB, VB, QJL>;
     auto load_step = [&](int64_t j0, regs & r) {
-        const uint32_t j = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(j0));  // wave-uniform
-        buf_dwords<4 * KB>(rk, vo_k, j * ks2 * kKcb, r.kw);
+        const int64_t j = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(j0 < w_end ? j0 : L));  // wave-uniform
+        const uint32_t left = static_cast<uint32_t>(L - j);  // tokens from j to L (0 past the end)
+        const int64_t kj = j * ks2, vj = j * vs2;
+        buf_dwords<4 * KB>(make_rsrc(kc0 + kj * kKcb, left * ks2 * kKcb), vo_k, 0, r.kw);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc0 + vj * kVcb, left * vs2 * kVcb);
 #pragma unroll
-        for (int hp = 0; hp < kPasses; ++hp) buf_dwords<VB>(rv, vo_v[hp], j * vs2 * kVcb, r.vw[hp]);
-        r.nk = __builtin_amdgcn_raw_buffer_load_b16(rkn, vo_kn, j * ks2 * 2, 0);
-        r.nv = __builtin_amdgcn_raw_buffer_load_b16(rvn, vo_vn, j * vs2 * 2, 0);
+        for (int hp = 0; hp < kPasses; ++hp) buf_dwords<VB>(rv, vo_v[hp], 0, r.vw[hp]);
+        r.nk = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(kn0 + kj, left * ks2 * 2), vo_kn, 0, 0);
+        r.nv = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(vn0 + vj, left * vs2 * 2), vo_vn, 0, 0);
         if constexpr (QJL) {
-            buf_dwords<4>(rks, vo_ks, j * ks2 * (kD / 8), r.ks);
-            r.kr = __builtin_amdgcn_raw_buffer_load_b16(rkr, vo_kn, j * ks2 * 2, 0);
+            buf_dwords<4>(make_rsrc(ks0 + kj * (kD / 8), left * ks2 * (kD / 8)), vo_ks, 0, r.ks);
+            r.kr = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(kr0 + kj, left * ks2 * 2), vo_kn, 0, 0);
         }
     };
 
@@ -461,8 +468,7 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     };
 
     // Ping-pong register sets: step i+1 loads into the set step i is not using.
-    // Loads are issued unconditionally (past the valid range a buffer load
-    // reads zeros or ignored positions) so that the wait counts stay static.
+    // Loads are issued for every step so that the wait counts stay static.
     for (int64_t j0 = w_begin; j0 < w_end; j0 += 2 * kStep) {
         load_step(j0 + kStep, r1);
         process(j0, r0);
@@ -563,10 +569,11 @@ bool attend_mfma_shape_ok(const dev_tables & kt, const dev_tables & vt, int32_t 
 bool attend_mfma_supported(const dev_tables & kt, const dev_tables & vt, const attend_args & a) {
     if (!attend_mfma_shape_ok(kt, vt, a.Hq, a.Hkv)) return false;
     if (a.chunk % (4 * kStep) != 0) return false;
-    // buffer offsets are 32-bit: the furthest byte of any plane of one (batch, head)
+    // buffer sizes and per-lane offsets are 32-bit: the furthest byte of any
+    // plane of one (batch, head), or of a step's 64 rows, stays below 2^31
     const int64_t row = kD * 4 / 8;  // widest code row (4 bits)
-    return a.t_max * a.k.stride[2] * row < (int64_t(1) << 31) &&
-           a.t_max * a.v.stride[2] * row < (int64_t(1) << 31);
+    const int64_t span = a.t_max + kStep;
+    return span * a.k.stride[2] * row < (int64_t(1) << 31) && span * a.v.stride[2] * row < (int64_t(1) << 31);
 }
 
 hipError_t launch_attend_mfma_partial(const dev_tables & kt, const dev_tables & vt, const attend_args & a,

@@ -1,0 +1,184 @@
+"""Summarise rocprofv3 output of bench.py into short text plus HBM traffic.
+
+    python -m kv_cache_quantization_05_amd.rocpd_summary --workload W \
+        --trace DIR [--fetch DIR --write DIR] --out-txt FILE [--traffic-json FILE] \
+        [--command "..."]
+
+--trace: a `rocprofv3 --kernel-trace --stats` run; --fetch / --write: runs of
+`rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` over `bench.py
+--calibrate-copy`.  The calibrating dispatch is the largest copy kernel of
+the run, which moves exactly 1 GiB; each counter is scaled by
+1 GiB / (its reading for that dispatch), so the reported bytes are in the
+units of a plain copy of known size.  Databases are deleted after reading
+(they are large); the text keeps the figures used.
+
+Launch groups: one tq_attend_decode call runs the split-K kernel, the merge
+kernel and (for QJL keys or the generic path) the query kernel, so its
+figures are sums over those kernels per merge dispatch; one tq_encode call
+runs one encode kernel, so its figures are averages over encode dispatches
+(K and V launches alike).
+"""
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import re
+import sqlite3
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+GIB = 1 << 30
+
+GROUPS = {
+    "attend_decode": re.compile(r"attend_mfma_kernel|attend_partial_kernel|attend_merge_kernel|query_prep_kernel"),
+    "encode": re.compile(r"encode_kernel|encode_qjl_kernel"),
+}
+# dispatches that count launches of each group
+ANCHORS = {"attend_decode": re.compile(r"attend_merge_kernel"), "encode": GROUPS["encode"]}
+
+
+def kernel_source_hash():
+    """Hash of the kernel sources; recorded traffic is valid only for it."""
+    h = hashlib.sha256()
+    csrc = os.path.join(PKG, "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def short(name):
+    name = re.sub(r"\(anonymous namespace\)::", "", name)
+    name = re.sub(r"\(.*", "", name)
+    return name.replace("void ", "")[-90:]
+
+
+def _dbs(d):
+    return sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))
+
+
+def read_trace(d):
+    rows = []
+    for db in _dbs(d):
+        con = sqlite3.connect(db)
+        rows += list(con.execute(
+            "select name, count(*), avg(duration)/1000.0, min(duration)/1000.0, max(duration)/1000.0, "
+            "max(vgpr_count), max(lds_size), max(scratch_size), "
+            "max(grid_x*grid_y*grid_z/(workgroup_x*workgroup_y*workgroup_z)) "
+            "from kernels group by name order by sum(duration) desc"))
+        con.close()
+    return rows
+
+
+def read_counter(d, counter):
+    """[(kernel, n, avg, max)] per kernel name, plus per-dispatch values of the
+    copy kernels (for calibration)."""
+    per, copies = [], []
+    for db in _dbs(d):
+        con = sqlite3.connect(db)
+        per += list(con.execute(
+            "select kernel_name, count(*), avg(value), max(value) from counters_collection "
+            "where counter_name = ? group by kernel_name", (counter,)))
+        copies += [r[0] for r in con.execute(
+            "select value from counters_collection where counter_name = ? and "
+            "(kernel_name like '%copyBuffer%' or kernel_name like '%copy_kernel%')", (counter,))]
+        con.close()
+    return per, copies
+
+
+def group_of(name):
+    for g, rx in GROUPS.items():
+        if rx.search(name):
+            return g
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--out-txt", required=True)
+    ap.add_argument("--traffic-json")
+    ap.add_argument("--command", default="")
+    ap.add_argument("--keep-db", action="store_true")
+    args = ap.parse_args()
+
+    out = [f"# rocprofv3 summary: workload {args.workload}", f"# kernel sources {kernel_source_hash()}"]
+    if args.command:
+        out.append(f"# commands: {args.command}")
+    trace = read_trace(args.trace)
+    out.append("## kernel trace (durations in us)")
+    out.append("kernel | calls | avg_us | min_us | max_us | vgpr | lds | scratch | blocks")
+    per_group = {}
+    for r in trace:
+        out.append(f"{short(r[0])} | {r[1]} | {r[2]:.2f} | {r[3]:.2f} | {r[4]:.2f} | {r[5]} | {r[6]} | {r[7]} | {r[8]}")
+        g = group_of(r[0])
+        if g:
+            per_group.setdefault(g, []).append((r[0], r[1], r[2]))
+    out.append("## per launch: total duration of the group's dispatches / launches")
+    launches = {}
+    for g, ks in per_group.items():
+        launches[g] = sum(k[1] for k in ks if ANCHORS[g].search(k[0]))
+        total = sum(k[1] * k[2] for k in ks)
+        out.append(f"{g}: {total / max(launches[g], 1):.2f} us per launch over {launches[g]} launches "
+                   f"({', '.join(f'{short(k[0])} x{k[1]}' for k in ks)})")
+
+    traffic = {}
+    for counter, d in (("FETCH_SIZE", args.fetch), ("WRITE_SIZE", args.write)):
+        if not d:
+            continue
+        per, copies = read_counter(d, counter)
+        if not copies or max(copies) <= 0:
+            out.append(f"## {counter}: no copy dispatch to calibrate against")
+            continue
+        cal = (GIB / 1024.0) / max(copies)  # KiB of a 1 GiB copy / counter reading
+        out.append(f"## {counter} (KiB per dispatch as read; calibration: the 1 GiB copy reads "
+                   f"{max(copies):.0f}, factor {cal:.4f})")
+        n_launch = {}
+        for k, n, avg, mx in sorted(per, key=lambda r: -r[2] * r[1]):
+            g = group_of(k)
+            if g is None and "copy" not in k.lower():
+                continue
+            out.append(f"{short(k)} | n={n} | avg={avg:.1f} | max={mx:.1f} | calibrated bytes/dispatch={avg * cal * 1024:.4g}")
+            if g:
+                traffic.setdefault(g, {}).setdefault(counter, 0.0)
+                traffic[g][counter] += n * avg * cal * 1024
+                if ANCHORS[g].search(k):
+                    n_launch[g] = n_launch.get(g, 0) + n
+        for g in traffic:
+            if counter in traffic[g]:
+                traffic[g][counter] /= max(n_launch.get(g, 1), 1)
+    if traffic:
+        out.append("## traffic per launch (calibrated bytes)")
+        for g, t in traffic.items():
+            out.append(f"{g}: fetch {t.get('FETCH_SIZE', 0):.4g} B, write {t.get('WRITE_SIZE', 0):.4g} B, "
+                       f"total {t.get('FETCH_SIZE', 0) + t.get('WRITE_SIZE', 0):.4g} B")
+    txt = "\n".join(out) + "\n"
+    os.makedirs(os.path.dirname(os.path.abspath(args.out_txt)), exist_ok=True)
+    with open(args.out_txt, "w") as f:
+        f.write(txt)
+    print(txt)
+    if args.traffic_json and traffic:
+        rec = {}
+        if os.path.exists(args.traffic_json):
+            rec = json.load(open(args.traffic_json))
+        for g, t in traffic.items():
+            if "FETCH_SIZE" in t and "WRITE_SIZE" in t:
+                rec[f"{args.workload}:{g}"] = {
+                    "bytes_per_launch": int(t["FETCH_SIZE"] + t["WRITE_SIZE"]),
+                    "fetch_bytes": int(t["FETCH_SIZE"]), "write_bytes": int(t["WRITE_SIZE"]),
+                    "source_hash": kernel_source_hash()}
+        with open(args.traffic_json, "w") as f:
+            json.dump(rec, f, indent=1, sort_keys=True)
+    if not args.keep_db:
+        for d in (args.trace, args.fetch, args.write):
+            if d:
+                for db in _dbs(d):
+                    os.remove(db)
+
+
+if __name__ == "__main__":
+    main()

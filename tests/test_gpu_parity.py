@@ -148,6 +148,33 @@ def test_attend_zero_and_clamped_lengths():
     assert_attend_close(o, ref)
 
 
+@pytest.mark.parametrize("kb,vb,qjl", [(3, 3, False), (4, 4, True)])
+def test_attend_ignores_slots_past_each_length(kb, vb, qjl):
+    # cache slots at or past a sequence's length hold garbage (0xFF bytes:
+    # NaN fp16 norms); they must not reach the output
+    d, B, Hkv, G, Tcap = 128, 3, 2, 4, 1500
+    kc = oenc.Config(seed=4, head_dim=d, bits=kb, qjl=qjl)
+    vc = oenc.Config(seed=4, head_dim=d, bits=vb)
+    rng = np.random.default_rng(5)
+    kp = _oracle_planes(rng.standard_normal((B, Hkv, Tcap, d)), kc)
+    vp = _oracle_planes(rng.standard_normal((B, Hkv, Tcap, d)), vc)
+    lens = np.array([1, 700, 1299], dtype=np.int32)
+    for planes in (kp, vp):
+        for name, arr in planes.items():
+            for b_, L in enumerate(lens):
+                arr[b_, :, L:] = np.iinfo(arr.dtype).max
+    q = rng.standard_normal((B, Hkv * G, d)).astype(np.float32)
+    ref = odec.attend_decode(q.astype(np.float64), kp, vp, kc, vc, lens)
+    kctx = tq.Context(seed=4, head_dim=d, bits=kb, qjl=qjl)
+    vctx = tq.Context(seed=4, head_dim=d, bits=vb)
+    out = tq.attend_decode(kctx, vctx, torch.from_numpy(q).to(DEV), tq.PackedPlanes.from_numpy(kp),
+                           tq.PackedPlanes.from_numpy(vp), torch.from_numpy(lens).to(DEV), t_max=Tcap)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(o))
+    _say("garbage past length", kb, vb, qjl, assert_attend_close(o, ref))
+
+
 @pytest.mark.parametrize("d,bits,qjl", [(128, 4, False), (128, 3, True), (256, 4, True), (32, 2, False)])
 def test_scores_full_matrix_matches_oracle(d, bits, qjl):
     cfg = oenc.Config(seed=3, head_dim=d, bits=bits, qjl=qjl)
