@@ -385,6 +385,243 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(const dev_tables t, con
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 input, MSE-only, d = 64 or 128: the rotation on matrix cores.
+//
+// H_d = H_(d/32) (x) H_32 (Sylvester order: the block index is the high bits
+// of the coordinate), so H_d D2 x is a 32-point transform of every block,
+// u_b = H_32 (D2 x)_b, followed by an (d/32)-point transform across blocks.
+// The 32-point part is a 16x16x32 bf16 MFMA per block and 16-row half, with
+// the inputs as the B operand exactly as loaded (bf16, D2 applied as sign
+// XORs) and H_32's +-1 entries as the A operand: products are exact and the
+// sums accumulate in fp32, as in the VALU butterflies.  A wave takes 16
+// vectors; lane l loads coordinates 8(l/16)..+7 of each block of vector
+// l%16.  The A rows are permuted so that the same lane receives output
+// coordinates 8(l/16)..+7 of each block: the cross-block transform, the
+// quantiser and the packing of 8 codes all stay in the lane.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) {
+    bf16x2 r;
+    __builtin_memcpy(&r, &w, 4);
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint32_t (&w)[4]) {
+    bf16x8 r;
+    __builtin_memcpy(&r, w, 16);
+    return r;
+}
+
+// 2c + bit, as one add-with-carry whose carry-in is the (per-lane) bit
+__device__ __forceinline__ uint32_t dbl_add(uint32_t c, bool bit) {
+    unsigned int co;
+    return __builtin_addc(c, c, bit ? 1u : 0u, &co);
+}
+
+template <int D, int BITS>
+__global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, const encode_args a,
+                                                          const grid_index gi, const uint32_t nvec) {
+    constexpr int NB = D / 32;
+    constexpr uint32_t kHalf = 1u << (BITS - 1);
+    constexpr uint32_t kAll = (1u << BITS) - 1;
+    static_assert(NB == 2 || NB == 4, "d = 64 or 128");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+
+    // A operand of output half tt: row m holds H_32 row 8(m/4) + 4 tt + m%4;
+    // this lane supplies row n, columns 8g..8g+7
+    uint32_t hw[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        const int row = 8 * (n >> 2) + 4 * tt + (n & 3);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c0 = 8 * g + 2 * j;
+            const uint32_t lo = (__builtin_popcount(row & c0) & 1) ? 0xBF80u : 0x3F80u;       // -1 / +1
+            const uint32_t hi = (__builtin_popcount(row & (c0 + 1)) & 1) ? 0xBF80u : 0x3F80u;
+            hw[tt][j] = lo | (hi << 16);
+        }
+    }
+    // the cross-block transform's signs go into the A operand: +-H_32 tiles
+    uint32_t hwn[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hwn[tt][j] = hw[tt][j] ^ 0x80008000u;
+    const bf16x8 hA[2][2] = {{as_bf16x8(hw[0]), as_bf16x8(hwn[0])}, {as_bf16x8(hw[1]), as_bf16x8(hwn[1])}};
+    // D2 as sign XORs of the loaded bf16 pairs
+    uint32_t m2[NB][4];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = 8 * g + 2 * j;
+            m2[b][j] = (((t.d2[b] >> e) & 1) << 15) | (((t.d2[b] >> (e + 1)) & 1) << 31);
+        }
+    // D1 (all bits of a code whose z changes sign) as XORs of the lane's
+    // 8-code chunks; and the chunk of a zero vector
+    uint32_t xm[NB], zero_chunk = 0;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        xm[b] = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xm[b] |= (((t.d1[b] >> (8 * g + j)) & 1) ? kAll : 0u) << (BITS * j);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) zero_chunk |= (kHalf - 1) << (BITS * j);
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = j < int(kHalf) - 1 ? t.th[kHalf + j] : 0.f;
+
+    // each wave takes 16 vectors per iteration
+    for (uint32_t base = blockIdx.x * 64 + wave * 16; base < nvec; base += gridDim.x * 64) {
+        const uint32_t v = base + n;
+        const bool valid = v < nvec;
+        int64_t xoff, pv;
+        vector_offsets(valid ? v : nvec - 1, a, gi, xoff, pv);
+
+        // inputs with D2 applied (sign XORs); the norm does not see the signs
+        uint32_t w[NB][4];
+        const uint16_t * src = static_cast<const uint16_t *>(a.x) + xoff + 8 * g;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(src + 32 * b);
+            w[b][0] = q.x ^ m2[b][0];
+            w[b][1] = q.y ^ m2[b][1];
+            w[b][2] = q.z ^ m2[b][2];
+            w[b][3] = q.w ^ m2[b][3];
+        }
+
+        // Norm, as float64 rounds it to fp16.  First in fp32 from exact bf16
+        // products (v_dot2): its error stays below 19 fp32 ulps of n (32
+        // roundings of positive partial sums, the lane sum and the square
+        // root), so unless n lies within 32 ulps of an fp16 rounding midpoint
+        // it rounds to the same fp16 as float64.  Those vectors, and norms
+        // outside fp16's normal range [2^-14, 60000] (where the midpoint test
+        // does not apply; products may also be subnormal), take the float64
+        // sum.  The 4 lanes of a vector hold bitwise-identical
+        // sums, so they decide alike.
+        float s32 = 0.f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s32 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[b][j]), as_bf16x2(w[b][j]), s32, false);
+        s32 += __shfl_xor(s32, 16);
+        s32 += __shfl_xor(s32, 32);
+        const float n32 = sqrtf(s32);
+        const int mid = int(__float_as_uint(n32) & 0x1FFFu) - 0x1000;
+        const bool exact64 = (mid > -32 && mid < 32) || !(n32 >= 0x1p-14f && n32 <= 60000.f);
+        double nrm = n32;
+        uint16_t nbits = static_cast<uint16_t>(__builtin_bit_cast(unsigned short, static_cast<_Float16>(n32)));
+        if (__any(exact64)) {
+            double nsq = 0.0;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const double lo = bf16_lo(w[b][j]), hi = bf16_hi(w[b][j]);
+                    nsq = fma(lo, lo, nsq);
+                    nsq = fma(hi, hi, nsq);
+                }
+            nsq += __shfl_xor(nsq, 16);
+            nsq += __shfl_xor(nsq, 32);
+            if (exact64) {
+                nrm = sqrt(nsq);
+                nbits = half_bits_rne(nrm);
+            }
+        }
+        if (valid && g == 0) a.out.norms[pv] = nbits;
+
+        // keep fp32 sums in range: rescale by a power of two (exact for bf16)
+        float nf = static_cast<float>(nrm);
+        const bool far = nrm > 0.0 && !(nrm >= 0x1p-60 && nrm <= 0x1p60);
+        if (__any(far)) {
+            const int e = far ? ilogb(nrm) : 0;
+            const float sc = ldexpf(1.f, -e);
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t lo = __float_as_uint(bf16_lo(w[b][j]) * sc) >> 16;
+                    const uint32_t hi = __float_as_uint(bf16_hi(w[b][j]) * sc) & 0xFFFF0000u;
+                    w[b][j] = lo | hi;
+                }
+            if (far) nf = static_cast<float>(ldexp(nrm, -e));
+        }
+
+        // y_b' = sum_b (-1)^popcount(b' & b) H_32 D2 x_b, all on matrix cores:
+        // lane gets coordinates 32 b' + 8 g + 4 tt + r of vector n
+        bf16x8 xb[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) xb[b] = as_bf16x8(w[b]);
+        // Codes of coordinates 32 b + 8 g + j, j = 4 tt + r, as 8-code chunks,
+        // built bit-serially from the top: chunk = 2 chunk + bit, each bit a
+        // compare result (code(z) = count of positive thresholds below |z|,
+        // with every bit flipped when z < 0, and 2^(b-1) set for z >= 0).
+        // One output block at a time keeps 8 accumulators live.
+        float T[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) T[j] = p[j] * nf;
+        uint8_t * const row = a.out.codes + pv * (D * BITS / 8);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            f32x4 u[2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int bi = 0; bi < NB; ++bi)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hA[tt][__builtin_popcount(b & bi) & 1], xb[bi], acc, 0, 0, 0);
+                u[tt] = acc;
+            }
+            uint32_t c = 0;
+#pragma unroll
+            for (int j = 7; j >= 0; --j) {
+                const float y = u[j >> 2][j & 3];
+                const float ya = fabsf(y);
+                const bool neg = y < 0.f;
+                c = dbl_add(c, !neg);
+                if constexpr (BITS == 4) {
+                    const bool t1 = ya > T[3];
+                    const float q2 = t1 ? T[5] : T[1];
+                    const float hi3 = t1 ? T[6] : T[2];
+                    const float lo3 = t1 ? T[4] : T[0];
+                    const bool t2 = ya > q2;
+                    const bool t3 = ya > (t2 ? hi3 : lo3);
+                    c = dbl_add(c, t1 != neg);
+                    c = dbl_add(c, t2 != neg);
+                    c = dbl_add(c, t3 != neg);
+                } else if constexpr (BITS == 3) {
+                    const bool t1 = ya > T[1];
+                    const bool t2 = ya > (t1 ? T[2] : T[0]);
+                    c = dbl_add(c, t1 != neg);
+                    c = dbl_add(c, t2 != neg);
+                } else {
+                    const bool t1 = ya > T[0];
+                    c = dbl_add(c, t1 != neg);
+                }
+            }
+            c = nrm > 0.0 ? c ^ xm[b] : zero_chunk;
+            if constexpr (BITS == 4) {
+                if (valid) reinterpret_cast<uint32_t *>(row + 16 * b)[g] = c;
+            } else if constexpr (BITS == 3) {
+                // block dword g = bits 32g..32g+31 = chunk g (24 bits at 24 g) and chunk g+1
+                const uint32_t nx = __shfl_down(c, 16);
+                const uint32_t dw = (c >> (8 * g)) | (nx << (24 - 8 * g));
+                if (valid && g < 3) reinterpret_cast<uint32_t *>(row + 12 * b)[g] = dw;
+            } else {
+                const uint32_t nx = __shfl_down(c, 16);
+                if (valid && (g & 1) == 0) reinterpret_cast<uint32_t *>(row + 8 * b)[g >> 1] = c | (nx << 16);
+            }
+        }
+    }
+}
+
 template <int D, int BITS, bool QJL>
 hipError_t launch_encode_dtype(const dev_tables & t, const encode_args & a, uint32_t nvec, hipStream_t s) {
     constexpr int VPB = 256 / (D / 32);
@@ -398,7 +635,12 @@ hipError_t launch_encode_dtype(const dev_tables & t, const encode_args & a, uint
         else
             hipLaunchKernelGGL((encode_qjl_kernel<D, BITS, false>), dim3(blocks), dim3(256), 0, s, t, a, gi, nvec);
     } else {
-        if (bf16)
+        if (bf16 && (D == 64 || D == 128)) {
+            constexpr int DM = D == 64 ? 64 : 128;
+            int64_t mb = (int64_t(nvec) + 63) / 64;
+            if (mb > 256 * 16) mb = 256 * 16;
+            hipLaunchKernelGGL((encode_mfma_kernel<DM, BITS>), dim3(mb), dim3(256), 0, s, t, a, gi, nvec);
+        } else if (bf16)
             hipLaunchKernelGGL((encode_kernel<D, BITS, true>), dim3(blocks), dim3(256), 0, s, t, a, gi, nvec);
         else
             hipLaunchKernelGGL((encode_kernel<D, BITS, false>), dim3(blocks), dim3(256), 0, s, t, a, gi, nvec);
