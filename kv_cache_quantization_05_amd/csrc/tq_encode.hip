@@ -24,8 +24,9 @@
 //    z, and the sign flips of D1 become one XOR with 2^b-1 per affected code
 //    on the packed words.  Comparing |y| against thresholds pre-multiplied
 //    by the norm avoids a per-coordinate division.
-//  * QJL ctx (encode_qjl_kernel): everything after the load in double, so
-//    that the fp16 residual norm also rounds exactly as float64 does.
+//  * QJL ctx (encode_qjl_kernel): the rotation, codes and residual in
+//    double, so that the fp16 residual norm also rounds exactly as float64
+//    does; the sketch S r on matrix cores (fp16 hi/lo split, ~22 bits).
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -287,101 +288,160 @@ __global__ __launch_bounds__(256) void encode_kernel(const dev_tables t, const e
     }
 }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f16x8 as_f16x8(uint4 w) {
+    f16x8 r;
+    __builtin_memcpy(&r, &w, 16);
+    return r;
+}
+
+// QJL ctx.  Phase A (per lane, one 32-coordinate block of one vector): the
+// rotation, z, codes, residual r = z - c[code] and gamma = ||r|| / sqrt(d) in
+// double (so gamma's fp16 rounding matches float64); r goes to LDS as an
+// fp16 hi + lo pair.  Phase B (per wave, a quarter of S's rows): the sketch
+// h = S r for the workgroup's vectors on matrix cores, 16x16x32 fp16 MFMAs
+// over S = S_hi + S_lo and r = r_hi + r_lo (three products; ~22 bits), and
+// the sign bits of h ([Orión plan] Fase 3; [TQ explainer] §2.2).  The sign
+// of S rho equals the sign of S r, rho = r / sqrt(d).
 template <int D, int BITS, bool BF16>
 __global__ __launch_bounds__(256) void encode_qjl_kernel(const dev_tables t, const encode_args a,
                                                          const grid_index gi, const uint32_t nvec) {
     constexpr int LPV = D / 32;
-    constexpr int VPB = 256 / LPV;
+    constexpr int VPB = 256 / LPV;   // vectors per workgroup iteration
     constexpr int NT = (1 << BITS) - 1;
+    constexpr int RS = D + 8;        // LDS row stride (halves): rows start 16 B apart in the banks
+    constexpr int RT = D / 16;       // 16-row tiles of S (m = d)
+    constexpr int KS = D / 32;       // 32-wide k-steps
+    constexpr int CT = VPB / 16;     // 16-vector column tiles
+    constexpr int CB = CT < 4 ? CT : 4;
+    __shared__ __align__(16) uint16_t rl[2][VPB * RS];
     const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int blk = tid % LPV;
+    const int vl = tid / LPV;        // vector within the workgroup's batch
     const uint32_t d1w = t.d1[blk];
     const uint32_t d2w = t.d2[blk];
     float th[NT];
 #pragma unroll
     for (int k = 0; k < NT; ++k) th[k] = t.th[k];
+    const uint16_t * const s_hi = t.S16;
+    const uint16_t * const s_lo = t.S16 + D * D;
 
     for (uint32_t base = blockIdx.x * VPB; base < nvec; base += gridDim.x * VPB) {
-        const uint32_t v = base + tid / LPV;
+        const uint32_t v = base + vl;
         const bool valid = v < nvec;
         int64_t xoff, pv;
         vector_offsets(valid ? v : nvec - 1, a, gi, xoff, pv);
 
+        // ---------------- phase A
         float xf[32];
         load_block<BF16>(a, xoff + blk * 32, xf);
         double x[32];
 #pragma unroll
         for (int e = 0; e < 32; ++e) x[e] = xf[e];
-
-        // norm of the input vector, float64 accumulation
         double nsq = 0.0;
 #pragma unroll
         for (int e = 0; e < 32; ++e) nsq = fma(x[e], x[e], nsq);
         nsq = group_sum<LPV>(nsq);
         const double n = sqrt(nsq);
         if (valid && blk == 0) a.out.norms[pv] = half_bits_rne(n);
-
-        // y = H . D2 . x  (unnormalised Hadamard)
 #pragma unroll
         for (int e = 0; e < 32; ++e)
             if ((d2w >> e) & 1) x[e] = -x[e];
         lane_fwht(x);
         cross_lane_fwht<LPV>(x, blk);
-
-        // z = sqrt(d) * R x / n = D1 . y / n ;  code = #{k : th_k < z}
+        // z = sqrt(d) R x / n = D1 y / n;  code = #{k : th_k < z}
         const double inv_n = n > 0.0 ? 1.0 / n : 0.0;
         uint32_t w[BITS];
 #pragma unroll
         for (int k = 0; k < BITS; ++k) w[k] = 0;
-        uint32_t codes[32];
+        double gsq = 0.0;
+        uint32_t rh[16], rlo[16];
 #pragma unroll
         for (int e = 0; e < 32; ++e) {
             double z = x[e] * inv_n;
             if ((d1w >> e) & 1) z = -z;
-            x[e] = z;
             uint32_t c = 0;
 #pragma unroll
             for (int k = 0; k < NT; ++k) c += (z > static_cast<double>(th[k])) ? 1u : 0u;
-            codes[e] = c;
             const int bit = BITS * e;
             w[bit >> 5] |= c << (bit & 31);
             if ((bit & 31) + BITS > 32) w[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
+            const double r = z - static_cast<double>(t.cb[c]);
+            gsq = fma(r, r, gsq);
+            const float rf = valid ? static_cast<float>(r) : 0.f;
+            const _Float16 h = static_cast<_Float16>(rf);
+            const _Float16 l = static_cast<_Float16>(rf - static_cast<float>(h));
+            const uint32_t hb = __builtin_bit_cast(unsigned short, h), lb = __builtin_bit_cast(unsigned short, l);
+            if (e & 1) {
+                rh[e >> 1] |= hb << 16;
+                rlo[e >> 1] |= lb << 16;
+            } else {
+                rh[e >> 1] = hb;
+                rlo[e >> 1] = lb;
+            }
         }
         if (valid) {
             uint32_t * dst = reinterpret_cast<uint32_t *>(a.out.codes + pv * (D * BITS / 8)) + blk * BITS;
 #pragma unroll
             for (int k = 0; k < BITS; ++k) dst[k] = w[k];
         }
-
-        // rho = (z - c[code]) / sqrt(d); gamma = ||rho||; signs of S rho
-        const double rs = 1.0 / sqrt(static_cast<double>(D));
-        float rho[32];
-        double gsq = 0.0;
-#pragma unroll
-        for (int e = 0; e < 32; ++e) {
-            const double rr = (x[e] - static_cast<double>(t.cb[codes[e]])) * rs;
-            gsq = fma(rr, rr, gsq);
-            rho[e] = static_cast<float>(rr);
-        }
         gsq = group_sum<LPV>(gsq);
-        if (valid && blk == 0) a.out.rnorms[pv] = half_bits_rne(sqrt(gsq));
-        // m == d rows: lane blk owns rows 32*blk .. 32*blk+31
-        uint32_t bits = 0;
-        for (int l = 0; l < D; ++l) {
-            const float4 * srow = reinterpret_cast<const float4 *>(t.S + int64_t(l) * D + blk * 32);
-            float acc = 0.f;
+        if (valid && blk == 0) a.out.rnorms[pv] = half_bits_rne(sqrt(gsq) / sqrt(static_cast<double>(D)));
+        {
+            uint4 * dh = reinterpret_cast<uint4 *>(&rl[0][vl * RS + 32 * blk]);
+            uint4 * dl = reinterpret_cast<uint4 *>(&rl[1][vl * RS + 32 * blk]);
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const float4 s4 = srow[c];
-                acc = fmaf(s4.x, rho[4 * c], acc);
-                acc = fmaf(s4.y, rho[4 * c + 1], acc);
-                acc = fmaf(s4.z, rho[4 * c + 2], acc);
-                acc = fmaf(s4.w, rho[4 * c + 3], acc);
+            for (int q = 0; q < 4; ++q) {
+                dh[q] = uint4{rh[4 * q], rh[4 * q + 1], rh[4 * q + 2], rh[4 * q + 3]};
+                dl[q] = uint4{rlo[4 * q], rlo[4 * q + 1], rlo[4 * q + 2], rlo[4 * q + 3]};
             }
-            acc = group_sum<LPV>(acc);
-            if ((l >> 5) == blk && acc > 0.f) bits |= 1u << (l & 31);
         }
-        if (valid) reinterpret_cast<uint32_t *>(a.out.signs + pv * (D / 8))[blk] = bits;
+        __syncthreads();
+
+        // ---------------- phase B: rows 16 rt .. +15 of h for 16 vectors per tile
+        const int n16 = lane & 15, g4 = lane >> 4;
+        for (int rt = wave; rt < RT; rt += 4) {
+#pragma unroll
+            for (int c0 = 0; c0 < CT; c0 += CB) {
+                f32x4 acc[CB];
+#pragma unroll
+                for (int c = 0; c < CB; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int64_t so = int64_t(16 * rt + n16) * D + 32 * ks + 8 * g4;
+                    const f16x8 ah = as_f16x8(*reinterpret_cast<const uint4 *>(s_hi + so));
+                    const f16x8 al = as_f16x8(*reinterpret_cast<const uint4 *>(s_lo + so));
+#pragma unroll
+                    for (int c = 0; c < CB; ++c) {
+                        const int ro = (16 * (c0 + c) + n16) * RS + 32 * ks + 8 * g4;
+                        const f16x8 bh = as_f16x8(*reinterpret_cast<const uint4 *>(&rl[0][ro]));
+                        const f16x8 bl = as_f16x8(*reinterpret_cast<const uint4 *>(&rl[1][ro]));
+                        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc[c], 0, 0, 0);
+                        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl, acc[c], 0, 0, 0);
+                        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc[c], 0, 0, 0);
+                    }
+                }
+                // lane holds rows 16 rt + 4 g4 + i of vector 16 (c0 + c) + n16
+#pragma unroll
+                for (int c = 0; c < CB; ++c) {
+                    uint32_t bits = 0;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) bits |= (acc[c][i] > 0.f ? 1u : 0u) << (4 * g4 + i);
+                    bits |= __shfl_xor(bits, 16);
+                    bits |= __shfl_xor(bits, 32);
+                    const uint32_t vv = base + 16 * (c0 + c) + n16;
+                    if (g4 == 0 && vv < nvec) {
+                        int64_t xo, pvv;
+                        vector_offsets(vv, a, gi, xo, pvv);
+                        reinterpret_cast<uint16_t *>(a.out.signs + pvv * (D / 8))[rt] = static_cast<uint16_t>(bits);
+                    }
+                }
+            }
+        }
+        __syncthreads();  // the residual tile is rewritten by the next iteration
     }
 }
 
@@ -400,7 +460,6 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(const dev_tables t, con
 // coordinates 8(l/16)..+7 of each block: the cross-block transform, the
 // quantiser and the packing of 8 codes all stay in the lane.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 

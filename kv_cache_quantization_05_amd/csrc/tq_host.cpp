@@ -129,18 +129,26 @@ int32_t tq_ctx_create(const tq_config * cfg, tq_ctx ** out) {
     c->tab.qjl = cfg->qjl;
     c->tab.S = nullptr;
     if (cfg->qjl) {
-        hipError_t e = hipMalloc(&c->S_dev, S.size() * sizeof(float));
+        // one allocation: S (fp32), then its fp16 split hi and lo
+        const size_t n = S.size();
+        std::vector<uint16_t> s16(2 * n);
+        tq::split_fp16(S.data(), static_cast<int64_t>(n), s16.data(), s16.data() + n);
+        const size_t bytes = n * sizeof(float) + 2 * n * sizeof(uint16_t);
+        hipError_t e = hipMalloc(&c->S_dev, bytes);
         if (e != hipSuccess) {
             delete c;
             return fail(TQ_STATUS_NO_MEMORY, "hipMalloc of S failed: %s", hipGetErrorString(e));
         }
-        e = hipMemcpy(c->S_dev, S.data(), S.size() * sizeof(float), hipMemcpyHostToDevice);
+        e = hipMemcpy(c->S_dev, S.data(), n * sizeof(float), hipMemcpyHostToDevice);
+        if (e == hipSuccess)
+            e = hipMemcpy(c->S_dev + n, s16.data(), 2 * n * sizeof(uint16_t), hipMemcpyHostToDevice);
         if (e != hipSuccess) {
             hipFree(c->S_dev);
             delete c;
             return device_status(e, "upload of S");
         }
         c->tab.S = c->S_dev;
+        c->tab.S16 = reinterpret_cast<const uint16_t *>(c->S_dev + n);
     }
     *out = c;
     return ok();

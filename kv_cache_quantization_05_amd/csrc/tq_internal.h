@@ -19,6 +19,7 @@ struct dev_tables {
     float cb[16];        // codebook, ascending; entries >= 2^b unused
     float th[16];        // 2^b - 1 thresholds; th[2^b - 1 ..] = +inf
     const float * S;     // device, m x d row-major (QJL only)
+    const uint16_t * S16;  // device, fp16 split of S: hi [m x d] then lo [m x d]
     int32_t d;
     int32_t bits;
     int32_t m;
@@ -29,6 +30,9 @@ struct dev_tables {
 int build_tables(const tq_config & cfg, int8_t * d1, int8_t * d2, float * codebook,
                  float * thresholds, float * s_rowmajor);
 int validate_config(const tq_config & cfg, const char ** why);
+// hi = fp16(v), lo = fp16(v - hi), both round-to-nearest-even (v ~ hi + lo
+// to ~2^-22 relative).
+void split_fp16(const float * v, int64_t n, uint16_t * hi, uint16_t * lo);
 
 // Launchers (kernel translation units).  Return hipError_t of the launch.
 struct encode_args {

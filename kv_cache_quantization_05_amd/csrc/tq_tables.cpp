@@ -97,6 +97,13 @@ std::vector<double> lloyd_max(int bits) {
 
 }  // namespace
 
+void split_fp16(const float * v, int64_t n, uint16_t * hi, uint16_t * lo) {
+    for (int64_t i = 0; i < n; ++i) {
+        hi[i] = half_bits_from_double(v[i]);
+        lo[i] = half_bits_from_double(static_cast<double>(v[i]) - half_bits_to_double(hi[i]));
+    }
+}
+
 int validate_config(const tq_config & cfg, const char ** why) {
     const int d = cfg.head_dim;
     if (d != 32 && d != 64 && d != 128 && d != 256) {
