@@ -175,6 +175,26 @@ def test_attend_ignores_slots_past_each_length(kb, vb, qjl):
     _say("garbage past length", kb, vb, qjl, assert_attend_close(o, ref))
 
 
+def test_attend_reuses_one_workspace():
+    # one workspace serves successive calls of different lengths
+    d, B, Hkv, G, T = 128, 2, 2, 4, 3000
+    kc = vc = oenc.Config(seed=9, head_dim=d, bits=3)
+    rng = np.random.default_rng(9)
+    kp = _oracle_planes(rng.standard_normal((B, Hkv, T, d)), kc)
+    vp = _oracle_planes(rng.standard_normal((B, Hkv, T, d)), vc)
+    q = rng.standard_normal((B, Hkv * G, d)).astype(np.float32)
+    ctx = tq.Context(seed=9, head_dim=d, bits=3)
+    kg, vg = tq.PackedPlanes.from_numpy(kp), tq.PackedPlanes.from_numpy(vp)
+    ws = torch.zeros(tq.attend_workspace_bytes(ctx, ctx, B, Hkv * G, Hkv, T), dtype=torch.uint8, device=DEV)
+    for lens in ([T, 17], [1, 2999], [0, 64], [T, T]):
+        lens = np.array(lens, dtype=np.int32)
+        ref = odec.attend_decode(q.astype(np.float64), kp, vp, kc, vc, lens)
+        out = tq.attend_decode(ctx, ctx, torch.from_numpy(q).to(DEV), kg, vg, torch.from_numpy(lens).to(DEV),
+                               t_max=T, workspace=ws)
+        torch.cuda.synchronize()
+        _say("workspace reuse", lens.tolist(), assert_attend_close(out.cpu().numpy().astype(np.float64), ref))
+
+
 @pytest.mark.parametrize("d,bits,qjl", [(128, 4, False), (128, 3, True), (256, 4, True), (32, 2, False)])
 def test_scores_full_matrix_matches_oracle(d, bits, qjl):
     cfg = oenc.Config(seed=3, head_dim=d, bits=bits, qjl=qjl)
