@@ -155,6 +155,7 @@ int32_t tq_encode(const struct tq_ctx * ctx, const void * x, int32_t x_dtype,
  * top_k in 1..64: out_scores [n_q, top_k] fp32 and out_idx [n_q, top_k] int64,
  * best first, equal scores ordered by lower index; the full score matrix is
  * never stored.  workspace: device memory of tq_scores_workspace() bytes.
+ * n_k is limited to 2^31 - 1 (TQ_STATUS_UNSUPPORTED beyond).
  */
 int32_t tq_scores(const struct tq_ctx * k_ctx, const float * q, int64_t n_q, float scale,
                   struct tq_planes k, int64_t n_k, int32_t top_k,

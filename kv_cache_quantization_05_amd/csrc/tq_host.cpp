@@ -186,8 +186,10 @@ int64_t tq_scores_workspace(const tq_ctx * k_ctx, int64_t n_q, int64_t n_k, int3
     if (!k_ctx || n_q < 0 || n_k < 0 || top_k < 0) return -1;
     const int64_t qp = round_up(n_q * (k_ctx->tab.d + k_ctx->tab.m) * 4);
     if (top_k == 0) return qp;
-    const int64_t ranges = tq::scores_ranges(n_k);
-    return qp + round_up(ranges * n_q * top_k * 4) + round_up(ranges * n_q * top_k * 8);
+    int32_t ranges = 1;
+    int64_t per = 0;
+    tq::scores_plan(k_ctx->tab.d, n_q, n_k, ranges, per);
+    return qp + round_up(int64_t(ranges) * n_q * top_k * 4) + round_up(int64_t(ranges) * n_q * top_k * 8);
 }
 
 int32_t tq_scores(const tq_ctx * k_ctx, const float * q, int64_t n_q, float scale, tq_planes k,
@@ -197,6 +199,7 @@ int32_t tq_scores(const tq_ctx * k_ctx, const float * q, int64_t n_q, float scal
     if (n_q < 0 || n_k < 0) return fail(TQ_STATUS_INVALID_ARG, "negative n_q or n_k");
     if (top_k < 0 || top_k > 64) return fail(TQ_STATUS_INVALID_ARG, "top_k must be in 0..64");
     if (top_k > 0 && top_k > n_k) return fail(TQ_STATUS_INVALID_ARG, "top_k exceeds n_k");
+    if (n_k > (int64_t(1) << 31) - 1) return fail(TQ_STATUS_UNSUPPORTED, "n_k is limited to 2^31 - 1");
     if (n_q == 0 || n_k == 0) return ok();
     if (!q || !out_scores) return fail(TQ_STATUS_INVALID_ARG, "q and out_scores must be non-NULL");
     if (top_k > 0 && !out_idx) return fail(TQ_STATUS_INVALID_ARG, "out_idx must be non-NULL when top_k > 0");
@@ -222,8 +225,8 @@ int32_t tq_scores(const tq_ctx * k_ctx, const float * q, int64_t n_q, float scal
     a.top_k = top_k;
     a.out_scores = out_scores;
     a.out_idx = out_idx;
+    tq::scores_plan(k_ctx->tab.d, n_q, n_k, a.n_ranges, a.keys_per_range);
     if (top_k > 0) {
-        a.n_ranges = tq::scores_ranges(n_k);
         char * p = ws + round_up(n_q * qp_stride * 4);
         a.cand_s = reinterpret_cast<float *>(p);
         a.cand_i = reinterpret_cast<int64_t *>(p + round_up(a.n_ranges * n_q * top_k * 4));

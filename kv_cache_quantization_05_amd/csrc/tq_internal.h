@@ -87,8 +87,10 @@ struct scores_args {
     float * cand_s;             // top-k candidates [n_ranges, n_q, top_k]
     int64_t * cand_i;
     int32_t n_ranges;
+    int64_t keys_per_range;     // keys of one range (a multiple of 16 on the matrix-core path)
 };
 hipError_t launch_scores(const dev_tables & t, const scores_args & a, hipStream_t s);
-int32_t scores_ranges(int64_t n_k);
+// Split of the keys into ranges (one block column each) for head_dim d.
+void scores_plan(int d, int64_t n_q, int64_t n_k, int32_t & ranges, int64_t & keys_per_range);
 
 }  // namespace tq

@@ -12,6 +12,7 @@
 
 #include "tq_device.h"
 #include "tq_internal.h"
+#include "tq_unpack.h"
 
 namespace tq {
 namespace {
@@ -265,8 +266,178 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(const scores_args a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core scorer, d = 128 or 256.  The score matrix of 16 queries x 16
+// keys is a real dense contraction: v_mfma_f32_16x16x32_f16 with the queries
+// as the A operand (held in registers for the whole key range: R q as fp16
+// hi + lo, ~22 bits, and S R q as fp16, whose contribution is scaled by
+// gamma sqrt(pi/2)/m and needs no more) and the keys as the B operand (fp16
+// centroids and +-1 signs, exact, unpacked with byte permutes).  Lane group g
+// (lanes 16g..16g+15) unpacks blocks d/128 g .. of its key, so a lane's key
+// is also the key of its output column: norms and gamma stay in the lane.
+// Top-k keeps a sorted list per query in LDS, touched only by scores that
+// reach the current k-th best.
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ half8 as_half8(const uint32_t * w) {
+    half8 h;
+    __builtin_memcpy(&h, w, 16);
+    return h;
+}
+
+// Insert (s, idx) into the sorted list (ls, li) of length K (one wave).
+__device__ __forceinline__ void wave_insert(float * ls, int32_t * li, int K, float s, int32_t idx, int lane) {
+    const float es = lane < K ? ls[lane] : -INFINITY;
+    const int32_t ei = lane < K ? li[lane] : INT32_MAX;
+    const bool ahead = lane < K && (es > s || (es == s && ei < idx));
+    const int pos = __popcll(__ballot(ahead));
+    const float ps = __shfl_up(es, 1);
+    const int32_t pi = __shfl_up(ei, 1);
+    if (pos < K && lane < K && lane >= pos) {
+        ls[lane] = lane == pos ? s : ps;
+        li[lane] = lane == pos ? idx : pi;
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+template <int D, int KB, bool QJL, bool TOPK>
+__global__ __launch_bounds__(64) void scores_mfma_kernel(const dev_tables t, const scores_args a) {
+    constexpr int NBL = D / 128;  // code blocks per lane group
+    constexpr int KS = 4 * NBL;   // k-steps (8 values per lane each)
+    __shared__ float lst_s[TOPK ? 16 : 1][64];
+    __shared__ int32_t lst_i[TOPK ? 16 : 1][64];
+    const int lane = threadIdx.x;
+    const int n16 = lane & 15, g = lane >> 4;
+    const int64_t q0 = int64_t(blockIdx.x) * 16;
+    const int64_t k_begin = int64_t(blockIdx.y) * a.keys_per_range;
+    const int64_t k_end = k_begin + a.keys_per_range < a.n_k ? k_begin + a.keys_per_range : a.n_k;
+
+    // A operands: query n16, values of the k-step order of the B operand
+    half8 aqh[KS], aql[KS], au[QJL ? KS : 1];
+    {
+        const int64_t qq = q0 + n16 < a.n_q ? q0 + n16 : a.n_q - 1;
+        const float * qrow = a.qp + qq * a.qp_stride;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int bl = NBL * g + ks / 4;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = qrow[32 * bl + block_code_of_pos<KB>(8 * (ks % 4) + e)];
+                const _Float16 hi = static_cast<_Float16>(x);
+                aqh[ks][e] = hi;
+                aql[ks][e] = static_cast<_Float16>(x - static_cast<float>(hi));
+                if constexpr (QJL) au[ks][e] = static_cast<_Float16>(qrow[D + 32 * bl + sign_bit_of_pos(8 * (ks % 4) + e)]);
+            }
+        }
+    }
+    const lut16 lut = make_lut(t.cb);
+    const float inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(D));
+    const float qjl_gain = sqrtf(0.5f * static_cast<float>(M_PI)) / static_cast<float>(D);
+    const int K = a.top_k;
+    float thr[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if constexpr (TOPK) {
+        for (int qi = 0; qi < 16; ++qi) {
+            lst_s[qi][lane] = -INFINITY;
+            lst_i[qi][lane] = INT32_MAX;
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    for (int64_t j0 = k_begin; j0 < k_end; j0 += 16) {
+        const int64_t key = j0 + n16;
+        const bool valid = key < k_end;
+        const int64_t kv = (valid ? key : k_end - 1) * a.k.stride[2];
+        uint32_t w[NBL * KB];
+        {
+            const uint32_t * crow = reinterpret_cast<const uint32_t *>(a.k.codes + kv * (D * KB / 8)) + NBL * KB * g;
+#pragma unroll
+            for (int i = 0; i < NBL * KB; ++i) w[i] = crow[i];
+        }
+        uint32_t sw[NBL];
+        if constexpr (QJL) {
+            const uint32_t * srow = reinterpret_cast<const uint32_t *>(a.k.signs + kv * (D / 8)) + NBL * g;
+#pragma unroll
+            for (int i = 0; i < NBL; ++i) sw[i] = srow[i];
+        }
+        const float nk = half_bits_to_float(a.k.norms[kv]);
+        const float gam = QJL ? half_bits_to_float(a.k.rnorms[kv]) * qjl_gain : 0.f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, accq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < NBL; ++b) {
+            uint32_t o[16];
+            unpack_block<KB>(lut, w + KB * b, o);
+#pragma unroll
+            for (int kq = 0; kq < 4; ++kq) {
+                const half8 bk = as_half8(o + 4 * kq);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aqh[4 * b + kq], bk, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aql[4 * b + kq], bk, acc, 0, 0, 0);
+            }
+            if constexpr (QJL) {
+                uint32_t so[16];
+                unpack_signs(sw[b], so);
+#pragma unroll
+                for (int kq = 0; kq < 4; ++kq)
+                    accq = __builtin_amdgcn_mfma_f32_16x16x32_f16(au[4 * b + kq], as_half8(so + 4 * kq), accq, 0, 0, 0);
+            }
+        }
+        // this lane: queries q0 + 4g + i (rows), key `key` (column n16)
+        float sc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[i] = a.scale * nk * (acc[i] * inv_sqrt_d + gam * accq[i]);
+        if constexpr (!TOPK) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t q = q0 + 4 * g + i;
+                if (valid && q < a.n_q) a.out_scores[q * a.n_k + key] = sc[i];
+            }
+        } else {
+            bool cand = false;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cand |= valid && sc[i] >= thr[i];
+            if (__any(cand)) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    uint64_t mask = __ballot(valid && sc[i] >= thr[i]);
+                    while (mask) {
+                        const int src = __builtin_ctzll(mask);
+                        mask &= mask - 1;
+                        const int qi = 4 * (src >> 4) + i;
+                        const float sv = __shfl(sc[i], src);
+                        const int32_t iv = static_cast<int32_t>(__shfl(static_cast<int32_t>(key), src));
+                        wave_insert(lst_s[qi], lst_i[qi], K, sv, iv, lane);
+                        if ((lane >> 4) == (src >> 4)) thr[i] = lst_s[qi][K - 1];
+                    }
+                }
+            }
+        }
+    }
+    if constexpr (TOPK) {
+        for (int qi = 0; qi < 16; ++qi) {
+            const int64_t q = q0 + qi;
+            if (q < a.n_q && lane < K) {
+                const int64_t o = (int64_t(blockIdx.y) * a.n_q + q) * K + lane;
+                a.cand_s[o] = lst_s[qi][lane];
+                a.cand_i[o] = lst_i[qi][lane] == INT32_MAX ? INT64_MAX : int64_t(lst_i[qi][lane]);
+            }
+        }
+    }
+}
+
 template <int D, int KB, bool QJL>
 hipError_t launch_scores_t(const dev_tables & t, const scores_args & a, hipStream_t s) {
+    if constexpr (D >= 128) {
+        const dim3 grid((a.n_q + 15) / 16, a.n_ranges);
+        if (a.top_k == 0) {
+            hipLaunchKernelGGL((scores_mfma_kernel<D, KB, QJL, false>), grid, dim3(64), 0, s, t, a);
+            return hipGetLastError();
+        }
+        hipLaunchKernelGGL((scores_mfma_kernel<D, KB, QJL, true>), grid, dim3(64), 0, s, t, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(topk_merge_kernel, dim3(a.n_q), dim3(64), 0, s, a);
+        return hipGetLastError();
+    }
     const int64_t qtiles = (a.n_q + kQT - 1) / kQT;
     if (a.top_k == 0) {
         dim3 grid((a.n_k + kKeys - 1) / kKeys, qtiles);
@@ -296,11 +467,29 @@ hipError_t launch_scores_d(const dev_tables & t, const scores_args & a, hipStrea
 
 }  // namespace
 
-int32_t scores_ranges(int64_t n_k) {
-    int64_t r = (n_k + 4095) / 4096;
-    if (r > 256) r = 256;
-    if (r < 1) r = 1;
-    return static_cast<int32_t>(r);
+// Matrix-core path (d >= 128): about 4096 waves in all (one per 16 queries
+// and range), at most 256 ranges (the final merge reads up to 4 lists per
+// lane), ranges a multiple of 16 keys.  VALU path: ranges of ~4096 keys.
+void scores_plan(int d, int64_t n_q, int64_t n_k, int32_t & ranges, int64_t & keys_per_range) {
+    int64_t r;
+    if (d >= 128) {
+        const int64_t qtiles = (n_q + 15) / 16;
+        r = (4096 + qtiles - 1) / qtiles;
+        const int64_t max_r = (n_k + 15) / 16;
+        if (r > max_r) r = max_r;
+        if (r > 256) r = 256;
+        if (r < 1) r = 1;
+        int64_t per = (n_k + r - 1) / r;
+        per = (per + 15) / 16 * 16;
+        keys_per_range = per;
+        r = (n_k + per - 1) / per;
+    } else {
+        r = (n_k + 4095) / 4096;
+        if (r > 256) r = 256;
+        if (r < 1) r = 1;
+        keys_per_range = (n_k + r - 1) / r;
+    }
+    ranges = static_cast<int32_t>(r < 1 ? 1 : r);
 }
 
 hipError_t launch_scores(const dev_tables & t, const scores_args & a, hipStream_t s) {
