@@ -16,7 +16,9 @@ Launch groups: one tq_attend_decode call runs the split-K kernel, the merge
 kernel and (for QJL keys or the generic path) the query kernel, so its
 figures are sums over those kernels per merge dispatch; one tq_encode call
 runs one encode kernel, so its figures are averages over encode dispatches
-(K and V launches alike).
+(K and V launches alike); one tq_scores call runs the query kernel, the
+scorer and (top-k) the list merge, counted per scorer dispatch.  The query
+kernel belongs to tq_scores in runs without decode kernels.
 """
 
 import argparse
@@ -32,10 +34,15 @@ GIB = 1 << 30
 
 GROUPS = {
     "attend_decode": re.compile(r"attend_mfma_kernel|attend_partial_kernel|attend_merge_kernel|query_prep_kernel"),
-    "encode": re.compile(r"encode_kernel|encode_qjl_kernel"),
+    "encode": re.compile(r"encode_kernel|encode_qjl_kernel|encode_mfma_kernel"),
+    "scores": re.compile(r"scores_mfma_kernel|scores_topk_kernel|scores_full_kernel|topk_merge_kernel"),
 }
 # dispatches that count launches of each group
-ANCHORS = {"attend_decode": re.compile(r"attend_merge_kernel"), "encode": GROUPS["encode"]}
+ANCHORS = {"attend_decode": re.compile(r"attend_merge_kernel"), "encode": GROUPS["encode"],
+           "scores": re.compile(r"scores_mfma_kernel|scores_topk_kernel|scores_full_kernel")}
+QUERY = re.compile(r"query_prep_kernel")
+DECODE_ONLY = re.compile(r"attend_mfma_kernel|attend_partial_kernel|attend_merge_kernel")
+_has_decode = [True]
 
 
 def kernel_source_hash():
@@ -88,6 +95,8 @@ def read_counter(d, counter):
 
 
 def group_of(name):
+    if QUERY.search(name) and not _has_decode[0]:
+        return "scores"
     for g, rx in GROUPS.items():
         if rx.search(name):
             return g
@@ -110,6 +119,7 @@ def main():
     if args.command:
         out.append(f"# commands: {args.command}")
     trace = read_trace(args.trace)
+    _has_decode[0] = any(DECODE_ONLY.search(r[0]) for r in trace)
     out.append("## kernel trace (durations in us)")
     out.append("kernel | calls | avg_us | min_us | max_us | vgpr | lds | scratch | blocks")
     per_group = {}
