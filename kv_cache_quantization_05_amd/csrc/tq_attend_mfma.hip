@@ -55,7 +55,7 @@ constexpr int kVRow = 2 * kD + 32;         // bytes per token row of the V tile 
 constexpr int kVTile = kPass * kVRow;      // 4608 B
 constexpr int kPTile = kStep * 8;          // 64 tokens x 4 heads x fp16
 constexpr int kWaveLds = kVTile + kPTile;
-constexpr float kSlack = 4.0f;
+constexpr float kSlack = 10.0f;  // w <= e^10 ~ 2.2e4 stays well inside fp16
 constexpr int kRsrcWord3 = 0x00020000;
 
 // Byte offset of token row r in a wave's V tile: rows are 288 B apart, with
@@ -137,16 +137,25 @@ __device__ __forceinline__ void buf_dwords(__amdgpu_buffer_rsrc_t r, uint32_t vo
     }
 }
 
-// 3-bit keys are decoded through a 64-entry LDS table indexed by two
-// consecutive codes (6 bits of the row's bit stream): entry e holds the fp16
-// centroids of codes e & 7 and e >> 3.  The table is stored 32 times, copy c
-// in bank c (entry e of copy c at byte 128 e + 4 c), and lane l reads copy
-// l % 32, so the 32 lanes served together never share a bank whatever codes
-// they hold.  A lookup costs a shift, a mask-or and one ds_read_b32 per two
-// codes.
-template <int KB>
-constexpr bool pair_table() { return KB == 3; }
+// 3-bit codes (keys and values alike) are decoded through a 64-entry LDS
+// table indexed by two consecutive codes (6 bits of the row's bit stream):
+// entry e holds the fp16 centroids of codes e & 7 and e >> 3.  The table is
+// stored 32 times, copy c in bank c (entry e of copy c at byte 128 e + 4 c),
+// and lane l reads copy l % 32, so the 32 lanes served together never share a
+// bank whatever codes they hold.  A lookup costs a shift, a mask-or and one
+// ds_read_b32 per two codes, and yields the pair in code order.
+template <int BITS>
+constexpr bool pair_table() { return BITS == 3; }
 constexpr int kPairCopies = 32;
+constexpr int kPairTabBytes = 64 * kPairCopies * 4;
+
+// Code index inside a 32-code block of output half `pos` as the decoder lays
+// the block out: pair-table look-ups keep code order, byte-permute unpacking
+// permutes it.
+template <int BITS>
+__host__ __device__ constexpr int decoded_code_of_pos(int pos) {
+    return pair_table<BITS>() ? pos : block_code_of_pos<BITS>(pos);
+}
 
 // LDS byte offset of pair p (codes 2p, 2p+1) of the code row held in w, in
 // the copy whose offset is lane_off.
@@ -183,12 +192,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 256), amdgpu_waves_per_
 void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
                                                           const attend_args a) {
     constexpr uint32_t kKcb = kD * KB / 8, kVcb = kD * VB / 8;
-    // one LDS array: the pair table (if any) at offset 0, so that its lookups
-    // need no base add, then the four waves' tiles
-    constexpr int kTabBytes = pair_table<KB>() ? 64 * kPairCopies * 4 : 0;
-    __shared__ __align__(16) uint8_t lds_all[kTabBytes + 4 * kWaveLds];
-    uint32_t * const ktab = reinterpret_cast<uint32_t *>(lds_all);
-    uint8_t * const lds = lds_all + kTabBytes;
+    // one LDS array: the key pair table (if any) at offset 0, so that its
+    // lookups need no base add, the value pair table (if any) at a constant
+    // offset folded into the reads, then the four waves' tiles
+    constexpr int kKTab = pair_table<KB>() ? kPairTabBytes : 0;
+    constexpr int kVTab = pair_table<VB>() ? kPairTabBytes : 0;
+    __shared__ __align__(16) uint8_t lds_all[kKTab + kVTab + 4 * kWaveLds];
+    uint8_t * const lds = lds_all + kKTab + kVTab;
+    uint32_t * const tabs = reinterpret_cast<uint32_t *>(lds_all);
+    const uint8_t * const tab_bytes = lds_all;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int lane = tid & 63;
@@ -253,12 +265,15 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     regs r0, r1;
     load_step(w_begin, r0);
 
-    if constexpr (pair_table<KB>()) {
-        for (int i = tid; i < 64 * kPairCopies; i += 256) {
-            const int e = i / kPairCopies;
-            ktab[i] = uint32_t(f16_bits(kt.cb[e & 7])) | (uint32_t(f16_bits(kt.cb[e >> 3])) << 16);
-        }
-    }
+    // pair tables: thread t writes copy t % 32 of entries t / 32 + 8 k, i.e.
+    // low half cb[t / 32], high half cb[k]
+    auto fill_pair_table = [&](const dev_tables & tb, uint32_t * tab) {
+        const uint32_t lo = f16_bits(tb.cb[tid >> 5]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) tab[tid + 256 * k] = lo | (uint32_t(f16_bits(tb.cb[k])) << 16);
+    };
+    if constexpr (pair_table<KB>()) fill_pair_table(kt, tabs);
+    if constexpr (pair_table<VB>()) fill_pair_table(vt, tabs + kKTab / 4);
 
     // ---- rotated queries.  MSE-only keys: each wave rotates its 4 heads
     // itself (q' = D1 H D2 q / sqrt(d), [TQ+ guide] §5.3): lane l holds
@@ -330,7 +345,7 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
             const int bl = gs >> 3, kk = gs & 7;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int kpos = pair_table<KB>() ? 4 * kk + i : block_code_of_pos<KB>(4 * kk + i);
+                const int kpos = decoded_code_of_pos<KB>(4 * kk + i);
                 const float x = qrow[32 * bl + kpos];
                 const _Float16 hi = static_cast<_Float16>(x);
                 aq[set][0][i] = hi;
@@ -346,6 +361,7 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     }
     const lut16 klut = make_lut(kt.cb);
     const lut16 vlut = make_lut(vt.cb);
+    const uint32_t lane_off = uint32_t(lane & 31) * 4;  // pair-table copy of this lane
     const float inv_sqrt_d = 1.0f / sqrtf(float(kD));
     const float kscale = a.scale * inv_sqrt_d;
     const float qjl_gain = sqrtf(0.5f * float(M_PI)) / float(kD) * sqrtf(float(kD));
@@ -366,18 +382,19 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     const int v_off = band_row * kVRow + (4 * (4 * (lane >> 4) + (lane & 3))) * 2;
 
     auto process = [&](int64_t j0, const regs & r) {
-        // ---------------- logits: lane l <- 4 heads of token j0 + l
-        floatx4 S = {0.f, 0.f, 0.f, 0.f};
+        // ---------------- logits: lane l <- 4 heads of token j0 + l.  Four
+        // independent accumulator chains (query hi / lo parts x even / odd
+        // k-steps) keep dependent MFMAs apart.
+        floatx4 Sc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         if constexpr (pair_table<KB>()) {
-            const uint8_t * tab = reinterpret_cast<const uint8_t *>(ktab);
-            const uint32_t lane_off = uint32_t(lane & 31) * 4;
+            const uint8_t * tab = tab_bytes;
 #pragma unroll
             for (int gs = 0; gs < 32; ++gs) {
                 const uint32_t lo = *reinterpret_cast<const uint32_t *>(tab + pair_offset(r.kw, 2 * gs, lane_off));
                 const uint32_t hi = *reinterpret_cast<const uint32_t *>(tab + pair_offset(r.kw, 2 * gs + 1, lane_off));
                 const half4 bk = as_half4(lo, hi);
-                S = mfma4_bcast(gs & 15, aq[gs >> 4][0], bk, S);
-                S = mfma4_bcast(gs & 15, aq[gs >> 4][1], bk, S);
+                Sc[2 * (gs & 1)] = mfma4_bcast(gs & 15, aq[gs >> 4][0], bk, Sc[2 * (gs & 1)]);
+                Sc[2 * (gs & 1) + 1] = mfma4_bcast(gs & 15, aq[gs >> 4][1], bk, Sc[2 * (gs & 1) + 1]);
             }
         } else {
 #pragma unroll
@@ -388,11 +405,12 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
                 for (int kk = 0; kk < 8; ++kk) {
                     const int gs = 8 * bl + kk;
                     const half4 bk = as_half4(bq[2 * kk], bq[2 * kk + 1]);
-                    S = mfma4_bcast(gs & 15, aq[gs >> 4][0], bk, S);
-                    S = mfma4_bcast(gs & 15, aq[gs >> 4][1], bk, S);
+                    Sc[2 * (gs & 1)] = mfma4_bcast(gs & 15, aq[gs >> 4][0], bk, Sc[2 * (gs & 1)]);
+                    Sc[2 * (gs & 1) + 1] = mfma4_bcast(gs & 15, aq[gs >> 4][1], bk, Sc[2 * (gs & 1) + 1]);
                 }
             }
         }
+        floatx4 S = (Sc[0] + Sc[2]) + (Sc[1] + Sc[3]);
         if constexpr (QJL) {
             floatx4 Sq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -427,7 +445,7 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
             const float lam = __logf(fmaxf(nv, 1e-26f));
 #pragma unroll
             for (int h = 0; h < kG; ++h) {
-                const float mn = fmaxf(mref[h], wave_max(s[h] + lam));
+                const float mn = fmaxf(mref[h], wave_max_uniform(s[h] + lam));
                 const float alpha = mref[h] == -INFINITY ? 0.f : __expf(mref[h] - mn);
                 mref[h] = mn;
                 lsum[h] *= alpha;
@@ -447,7 +465,13 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
         for (int hp = 0; hp < kPasses; ++hp) {
             {
                 uint32_t o[16];
-                unpack_block<VB>(vlut, r.vw[hp], o);
+                if constexpr (pair_table<VB>()) {
+#pragma unroll
+                    for (int p = 0; p < 16; ++p)
+                        o[p] = *reinterpret_cast<const uint32_t *>(tab_bytes + kKTab + pair_offset(r.vw[hp], p, lane_off));
+                } else {
+                    unpack_block<VB>(vlut, r.vw[hp], o);
+                }
                 uint8_t * dst = vtile + vrow_off(lane & 15) + (lane >> 4) * 64;
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
@@ -469,7 +493,17 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
 
     // Ping-pong register sets: step i+1 loads into the set step i is not using.
     // Loads are issued for every step so that the wait counts stay static.
+    // Waves sharing a SIMD are otherwise served oldest first, which leaves the
+    // youngest finishing alone; a wave drops its issue priority by one level
+    // per quarter of its range done, so lagging waves catch up.
+    const int64_t span = w_end > w_begin ? w_end - w_begin : 1;
     for (int64_t j0 = w_begin; j0 < w_end; j0 += 2 * kStep) {
+        switch (static_cast<int>((j0 - w_begin) * 4 / span)) {
+            case 0: __builtin_amdgcn_s_setprio(3); break;
+            case 1: __builtin_amdgcn_s_setprio(2); break;
+            case 2: __builtin_amdgcn_s_setprio(1); break;
+            default: __builtin_amdgcn_s_setprio(0); break;
+        }
         load_step(j0 + kStep, r1);
         process(j0, r0);
         if (j0 + kStep >= w_end) break;
@@ -485,7 +519,7 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
 #pragma unroll
     for (int dh = 0; dh < 2; ++dh) {
         const int c = 64 * dh + 4 * (lane >> 2) + (lane & 3);  // V tile column -> rotated-domain dim
-        const int dim = 32 * (c >> 5) + block_code_of_pos<VB>(c & 31);
+        const int dim = 32 * (c >> 5) + decoded_code_of_pos<VB>(c & 31);
 #pragma unroll
         for (int h = 0; h < kG; ++h) res[h * (kD + 2) + 2 + dim] = acc[dh][h];
     }

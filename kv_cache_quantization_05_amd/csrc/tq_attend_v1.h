@@ -231,82 +231,111 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(const dev_tables kt
 }
 
 // Log-sum-exp merge of the per-chunk states of one (batch, query head), then
-// the inverse rotation o = R^T o' back to the original domain.  Two passes:
-// the block's 256 threads find the largest chunk maximum M, then wave w
-// accumulates chunks w, w+4, ... weighted by exp(m_c - M) (lane = dims
-// lane, lane+64, ...), with several chunks' loads in flight, and the four
-// waves' sums are added through LDS.
+// the inverse rotation o = R^T o' back to the original domain.  One pass:
+// wave w owns chunks [32 w, 32 w + 32), [32 w + 128, ...), ...; each batch's
+// loads (m, l and the lane's dims lane + 64 i of every chunk) are all issued
+// before any is used, and the wave keeps a running maximum.  The four waves'
+// states are combined through LDS, and wave 0 applies R^T with the
+// Walsh-Hadamard butterflies run across lanes (no block barriers).
 template <int D>
 __global__ __launch_bounds__(256) void attend_merge_kernel(const dev_tables vt, const attend_args a) {
-    constexpr int PER = D >= 64 ? D / 64 : 1;
-    __shared__ float red[4];
-    __shared__ float part_acc[4][D];
-    __shared__ float part_l[4];
-    __shared__ float s[D];
+    constexpr int PER = D >= 64 ? D / 64 : 1;  // dims per lane
+    constexpr int CB = 32;                     // chunks per wave per batch
+    __shared__ float wm[4], wl[4];
+    __shared__ float wacc[4][PER * 64];
     const int h = blockIdx.x, b = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float * base = a.partial + (int64_t(b) * a.Hq + h) * a.n_chunks * (D + 2);
     const int n = a.n_chunks;
-    float m = -INFINITY;
-    for (int c = tid; c < n; c += 256) m = fmaxf(m, base[int64_t(c) * (D + 2)]);
-    m = wave_max(m);
-    if (lane == 0) red[wave] = m;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    float acc[PER], l = 0.f;
+    float M = -INFINITY, l = 0.f, acc[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-    if (M != -INFINITY) {
-        constexpr int U = 8;  // chunks per batch of loads
-        for (int c0 = wave; c0 < n; c0 += 4 * U) {
-            float mc[U], lc[U], vc[U][PER];
+    for (int c0 = wave * CB; c0 < n; c0 += 4 * CB) {
+        float mc[CB], lc[CB], vc[CB][PER];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = c0 + 4 * u;
-                const float * p = base + int64_t(c < n ? c : c0) * (D + 2);
-                mc[u] = c < n ? p[0] : -INFINITY;
-                lc[u] = p[1];
+        for (int u = 0; u < CB; ++u) {
+            const int c = c0 + u;
+            const float * p = base + int64_t(c < n ? c : c0) * (D + 2);
+            mc[u] = c < n ? p[0] : -INFINITY;
+            lc[u] = p[1];
 #pragma unroll
-                for (int i = 0; i < PER; ++i) vc[u][i] = (lane + 64 * i < D) ? p[2 + lane + 64 * i] : 0.f;
-            }
+            for (int i = 0; i < PER; ++i) vc[u][i] = (lane + 64 * i < D) ? p[2 + lane + 64 * i] : 0.f;
+        }
+        float mb = M;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const float w = mc[u] == -INFINITY ? 0.f : __expf(mc[u] - M);
+        for (int u = 0; u < CB; ++u) mb = fmaxf(mb, mc[u]);
+        if (mb != -INFINITY) {
+            const float sc = M == -INFINITY ? 0.f : __expf(M - mb);
+            l *= sc;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) acc[i] *= sc;
+#pragma unroll
+            for (int u = 0; u < CB; ++u) {
+                const float w = mc[u] == -INFINITY ? 0.f : __expf(mc[u] - mb);
                 l = fmaf(w, lc[u], l);
 #pragma unroll
                 for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, vc[u][i], acc[i]);
             }
+            M = mb;
         }
     }
+    if (lane == 0) {
+        wm[wave] = M;
+        wl[wave] = l;
+    }
 #pragma unroll
-    for (int i = 0; i < PER; ++i)
-        if (lane + 64 * i < D) part_acc[wave][lane + 64 * i] = acc[i];
-    if (lane == 0) part_l[wave] = l;
+    for (int i = 0; i < PER; ++i) wacc[wave][lane + 64 * i] = acc[i];
     __syncthreads();
-    const float Lsum = part_l[0] + part_l[1] + part_l[2] + part_l[3];
-    if (tid < D) {
-        const float o0 = part_acc[0][tid] + part_acc[1][tid] + part_acc[2][tid] + part_acc[3][tid];
-        float o = o0;
-        o = (M != -INFINITY && Lsum > 0.f) ? o / Lsum : 0.f;
+    if (wave != 0) return;
+    const float Mx = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+    float sw[4], L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        sw[w] = wm[w] == -INFINITY ? 0.f : __expf(wm[w] - Mx);
+        L = fmaf(sw[w], wl[w], L);
+    }
+    const bool ok = Mx != -INFINITY && L > 0.f;
+    const float inv = ok ? 1.0f / L : 0.f;
+    float x[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int dim = lane + 64 * i;
+        float o = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) o = fmaf(sw[w], wacc[w][dim], o);
+        o *= inv;
         // o_orig = R^T o = D2 . H . D1 . o / sqrt(d)
-        if ((vt.d1[tid >> 5] >> (tid & 31)) & 1) o = -o;
-        s[tid] = o;
+        if (dim < D && ((vt.d1[dim >> 5] >> (dim & 31)) & 1)) o = -o;
+        x[i] = dim < D ? o : 0.f;
     }
+    // butterflies: strides of 64 and up inside the lane, below 64 across lanes
 #pragma unroll
-    for (int hh = 1; hh < D; hh <<= 1) {
-        __syncthreads();
-        if (tid < D && (tid & hh) == 0) {
-            const float x = s[tid], y = s[tid + hh];
-            s[tid] = x + y;
-            s[tid + hh] = x - y;
+    for (int hh = 1; hh < PER; hh <<= 1)
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            if ((i & hh) == 0) {
+                const float u = x[i], v = x[i + hh];
+                x[i] = u + v;
+                x[i + hh] = u - v;
+            }
+    constexpr int LANES = D >= 64 ? 64 : D;
+#pragma unroll
+    for (int hh = 1; hh < LANES; hh <<= 1)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const float pv = __shfl_xor(x[i], hh);
+            x[i] = (lane & hh) ? pv - x[i] : x[i] + pv;
         }
-    }
-    __syncthreads();
-    if (tid < D) {
-        float y = s[tid] * (1.0f / sqrtf(static_cast<float>(D)));
-        if ((vt.d2[tid >> 5] >> (tid & 31)) & 1) y = -y;
-        a.out[(int64_t(b) * a.Hq + h) * D + tid] = y;
+    const float rs = 1.0f / sqrtf(static_cast<float>(D));
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int dim = lane + 64 * i;
+        if (dim < D) {
+            float y = x[i] * rs;
+            if ((vt.d2[dim >> 5] >> (dim & 31)) & 1) y = -y;
+            a.out[(int64_t(b) * a.Hq + h) * D + dim] = y;
+        }
     }
 }
 

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace tq {
 
 // ---------------------------------------------------------------------------
@@ -51,6 +53,26 @@ __device__ __forceinline__ T group_sum(T v) {
 __device__ __forceinline__ float wave_max(float v) {
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
     return v;
+}
+
+// Maximum over the wave, returned wave-uniform: DPP max within each row of 16
+// lanes (quad swaps, then half-row and row mirrors), then the four row results
+// read into scalars.
+__device__ __forceinline__ float wave_max_uniform(float v) {
+    auto dpp_max = [](float x, auto ctrl) {
+        const int y = __builtin_amdgcn_mov_dpp(__float_as_int(x), decltype(ctrl)::value, 0xF, 0xF, false);
+        return fmaxf(x, __int_as_float(y));
+    };
+    v = dpp_max(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+    v = dpp_max(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+    v = dpp_max(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+    v = dpp_max(v, std::integral_constant<int, 0x140>{});  // row_mirror
+    const int b = __float_as_int(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
