@@ -481,7 +481,7 @@ __device__ __forceinline__ uint32_t dbl_add(uint32_t c, bool bit) {
     return __builtin_addc(c, c, bit ? 1u : 0u, &co);
 }
 
-template <int D, int BITS>
+template <int D, int BITS, bool PREFETCH>
 __global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, const encode_args a,
                                                           const grid_index gi, const uint32_t nvec) {
     constexpr int NB = D / 32;
@@ -537,24 +537,40 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, co
 #pragma unroll
     for (int j = 0; j < 8; ++j) p[j] = j < int(kHalf) - 1 ? t.th[kHalf + j] : 0.f;
 
-    // each wave takes 16 vectors per iteration
-    for (uint32_t base = blockIdx.x * 64 + wave * 16; base < nvec; base += gridDim.x * 64) {
-        const uint32_t v = base + n;
-        const bool valid = v < nvec;
-        int64_t xoff, pv;
-        vector_offsets(valid ? v : nvec - 1, a, gi, xoff, pv);
-
-        // inputs with D2 applied (sign XORs); the norm does not see the signs
-        uint32_t w[NB][4];
+    // each wave takes 16 vectors per iteration; with PREFETCH the next
+    // iteration's inputs are loaded while the current ones are processed
+    const uint32_t stride = gridDim.x * 64;
+    uint32_t wn[NB][4];
+    int64_t pv_next = 0;
+    bool valid_next = false;
+    auto load_inputs = [&](uint32_t bs) {
+        const uint32_t v = bs + n;
+        valid_next = v < nvec;
+        int64_t xoff;
+        vector_offsets(valid_next ? v : nvec - 1, a, gi, xoff, pv_next);
         const uint16_t * src = static_cast<const uint16_t *>(a.x) + xoff + 8 * g;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const uint4 q = *reinterpret_cast<const uint4 *>(src + 32 * b);
-            w[b][0] = q.x ^ m2[b][0];
-            w[b][1] = q.y ^ m2[b][1];
-            w[b][2] = q.z ^ m2[b][2];
-            w[b][3] = q.w ^ m2[b][3];
+            wn[b][0] = q.x;
+            wn[b][1] = q.y;
+            wn[b][2] = q.z;
+            wn[b][3] = q.w;
         }
+    };
+    uint32_t base = blockIdx.x * 64 + wave * 16;
+    if (PREFETCH && base < nvec) load_inputs(base);
+    for (; base < nvec; base += stride) {
+        if (!PREFETCH) load_inputs(base);
+        const bool valid = valid_next;
+        const int64_t pv = pv_next;
+        // inputs with D2 applied (sign XORs); the norm does not see the signs
+        uint32_t w[NB][4];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w[b][j] = wn[b][j] ^ m2[b][j];
+        if (PREFETCH && base + stride < nvec) load_inputs(base + stride);
 
         // Norm, as float64 rounds it to fp16.  First in fp32 from exact bf16
         // products (v_dot2): its error stays below 19 fp32 ulps of n (32
@@ -696,9 +712,28 @@ hipError_t launch_encode_dtype(const dev_tables & t, const encode_args & a, uint
     } else {
         if (bf16 && (D == 64 || D == 128)) {
             constexpr int DM = D == 64 ? 64 : 128;
-            int64_t mb = (int64_t(nvec) + 63) / 64;
-            if (mb > 256 * 16) mb = 256 * 16;
-            hipLaunchKernelGGL((encode_mfma_kernel<DM, BITS>), dim3(mb), dim3(256), 0, s, t, a, gi, nvec);
+            // Up to 4 iterations per resident block: one round of blocks,
+            // each taking the same number of 64-vector iterations, with the
+            // next iteration's inputs prefetched.  Larger inputs: a fixed grid
+            // striding over the vectors, loading at each iteration's start.
+            static int cap = 0;
+            if (cap == 0) {
+                int dev = 0, per_cu = 0;
+                hipDeviceProp_t prop;
+                const bool ok = hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+                                hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, encode_mfma_kernel<DM, BITS, true>,
+                                                                             256, 0) == hipSuccess;
+                cap = ok && per_cu > 0 ? prop.multiProcessorCount * per_cu : 256 * 4;
+            }
+            const int64_t need = (int64_t(nvec) + 63) / 64;
+            const int64_t iters = (need + cap - 1) / cap;
+            if (iters <= 4) {
+                const int64_t mb = (need + iters - 1) / iters;
+                hipLaunchKernelGGL((encode_mfma_kernel<DM, BITS, true>), dim3(mb), dim3(256), 0, s, t, a, gi, nvec);
+            } else {
+                const int64_t mb = need < 256 * 16 ? need : 256 * 16;
+                hipLaunchKernelGGL((encode_mfma_kernel<DM, BITS, false>), dim3(mb), dim3(256), 0, s, t, a, gi, nvec);
+            }
         } else if (bf16)
             hipLaunchKernelGGL((encode_kernel<D, BITS, true>), dim3(blocks), dim3(256), 0, s, t, a, gi, nvec);
         else
