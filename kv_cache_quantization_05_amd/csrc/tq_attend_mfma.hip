@@ -51,24 +51,27 @@ constexpr int kG = 4;
 constexpr int kStep = 64;                  // tokens per wave iteration (one per lane)
 constexpr int kPass = 16;                  // tokens per V tile pass
 constexpr int kPasses = kStep / kPass;
-constexpr int kVRow = 2 * kD + 32;         // bytes per token row of the V tile (padded)
-constexpr int kVTile = kPass * kVRow;      // 4608 B
+constexpr int kStage = kG * kD * 4;       // rotated queries (prologue) / wave results (epilogue)
 constexpr int kPTile = kStep * 8;          // 64 tokens x 4 heads x fp16
-constexpr int kWaveLds = kVTile + kPTile;
+constexpr int kWaveLds = kStage + kPTile;
+static_assert(kG * (kD + 2) * 4 <= kWaveLds, "wave results fit the wave's LDS");
 constexpr float kSlack = 10.0f;  // w <= e^10 ~ 2.2e4 stays well inside fp16
 constexpr int kRsrcWord3 = 0x00020000;
-
-// Byte offset of token row r in a wave's V tile: rows are 288 B apart, with
-// 16 B more for rows with bit 2 set.  The 8 rows written together by 16-byte
-// stores start in 8 distinct 16-byte bank slots, and the 4 rows read together
-// by ds_read_b64_tr_b16 cover 128 bytes of banks exactly once; offsets stay
-// affine in the column, so they fold into instruction offsets.
-__device__ __forceinline__ int vrow_off(int r) { return r * kVRow + ((r >> 2) & 1) * 16; }
 
 __device__ __forceinline__ half4 tr_read4(const uint8_t * lds_base, int off) {
     const shortx4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(lds_base + off));
     half4 h;
     __builtin_memcpy(&h, &a, 8);
+    return h;
+}
+
+// Four fp32 values that are exact in fp16 -> half4 (round toward zero is exact).
+__device__ __forceinline__ half4 to_half4(floatx4 c) {
+    const auto lo = __builtin_amdgcn_cvt_pkrtz(c[0], c[1]);
+    const auto hi = __builtin_amdgcn_cvt_pkrtz(c[2], c[3]);
+    half4 h;
+    __builtin_memcpy(&h, &lo, 4);
+    __builtin_memcpy(reinterpret_cast<char *>(&h) + 4, &hi, 4);
     return h;
 }
 
@@ -180,11 +183,13 @@ struct step_regs {
     uint16_t nk, nv;         // K and V norms of token lane
 };
 
-// Waves per SIMD the register budget is sized for: 4 (at most 128 VGPRs) where
-// the loop still fits without spilling, else the compiler's choice.
+// Waves per SIMD the register budget is sized for: 3 (at most 168 VGPRs) for
+// the common 3-bit MSE-only case, else the compiler's choice.  Throughput
+// barely depends on occupancy here (one wave per SIMD already reaches most of
+// it), so registers go to the pipelined step data and accumulators.
 template <int KB, int VB, bool QJL>
 constexpr int waves_per_simd() {
-    return (!QJL && VB == 3 && KB <= 3) ? 4 : 1;
+    return (!QJL && VB == 3 && KB <= 3) ? 3 : 1;
 }
 
 template <int KB, int VB, bool QJL>
@@ -205,8 +210,8 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int lane = tid & 63;
     const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    uint8_t * vtile = lds + wave * kWaveLds;
-    uint8_t * ptile = vtile + kVTile;
+    uint8_t * stage = lds + wave * kWaveLds;
+    uint8_t * ptile = stage + kStage;
 
     int64_t L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
     L = L < 0 ? 0 : (L > a.t_max ? a.t_max : L);
@@ -242,7 +247,7 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     uint32_t vo_v[kPasses];
 #pragma unroll
     for (int hp = 0; hp < kPasses; ++hp)
-        vo_v[hp] = uint32_t(kPass * hp + (lane & 15)) * vs2 * kVcb + (lane >> 4) * 4 * VB;
+        vo_v[hp] = uint32_t(kPass * hp + 4 * (lane >> 4) + (lane & 3)) * vs2 * kVcb + ((lane >> 2) & 3) * 4 * VB;
 
     using regs = step_regs<KB, VB, QJL>;
     auto load_step = [&](int64_t j0, regs & r) {
@@ -324,10 +329,10 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
         const float rs = 1.0f / sqrtf(float(kD));
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = ((s1 >> i) & 1) ? -v[i] * rs : v[i] * rs;
-        float4 * dst = reinterpret_cast<float4 *>(vtile + (h * kD + e0) * 4);
+        float4 * dst = reinterpret_cast<float4 *>(stage + (h * kD + e0) * 4);
         dst[0] = float4{v[0], v[1], v[2], v[3]};
         dst[1] = float4{v[4], v[5], v[6], v[7]};
-        qsrc = reinterpret_cast<const float *>(vtile);
+        qsrc = reinterpret_cast<const float *>(stage);
         qstride = kD;
     } else {
         qsrc = a.qp + (int64_t(b) * a.Hq + g * kG) * a.qp_stride;
@@ -367,7 +372,11 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     const float qjl_gain = sqrtf(0.5f * float(M_PI)) / float(kD) * sqrtf(float(kD));
     const float w_cap = __expf(kSlack);
 
-    floatx4 acc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+    // acc[gd]: heads x dim (32 blk + 4 gd + (lane & 3)), blk = (lane >> 2) & 3,
+    // summed over the tokens of quad lane >> 4 of every pass
+    floatx4 acc[8];
+#pragma unroll
+    for (int gd = 0; gd < 8; ++gd) acc[gd] = floatx4{0.f, 0.f, 0.f, 0.f};
     float mref[kG], lsum[kG];
 #pragma unroll
     for (int h = 0; h < kG; ++h) {
@@ -375,11 +384,13 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
         lsum[h] = 0.f;
     }
 
-    // transposed-read addresses (fixed per lane): lane j of each 16-lane group
-    // points at row j/4 of a 4-row band, column group j%4
-    const int band_row = (lane & 15) >> 2;
-    const int p_off = band_row * 8;
-    const int v_off = band_row * kVRow + (4 * (4 * (lane >> 4) + (lane & 3))) * 2;
+    // transposed read of the weights: lane j of 16-lane group q points at
+    // token 4 q + j / 4 of the pass and receives head j % 4 of the quad's 4
+    // tokens (the A operand of blocks 4 q .. 4 q + 3)
+    const int p_off = (4 * (lane >> 4) + ((lane & 15) >> 2)) * 8;
+    // 4x4 identity as the B operand: lane 4 b + n holds column n
+    const half4 ident = as_half4((lane & 3) == 0 ? 0x3C00u : (lane & 3) == 1 ? 0x3C000000u : 0u,
+                                 (lane & 3) == 2 ? 0x3C00u : (lane & 3) == 3 ? 0x3C000000u : 0u);
 
     auto process = [&](int64_t j0, const regs & r) {
         // ---------------- logits: lane l <- 4 heads of token j0 + l.  Four
@@ -449,8 +460,8 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
                 const float alpha = mref[h] == -INFINITY ? 0.f : __expf(mref[h] - mn);
                 mref[h] = mn;
                 lsum[h] *= alpha;
-                acc[0][h] *= alpha;
-                acc[1][h] *= alpha;
+#pragma unroll
+                for (int gd = 0; gd < 8; ++gd) acc[gd][h] *= alpha;
                 p[h] = __expf(s[h] - mn);
             }
         }
@@ -460,33 +471,27 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
             u32x2{uint32_t(f16_bits(p[0] * nv)) | (uint32_t(f16_bits(p[1] * nv)) << 16),
                   uint32_t(f16_bits(p[2] * nv)) | (uint32_t(f16_bits(p[3] * nv)) << 16)};
 
-        // ---------------- values, 16 tokens per pass through the LDS tile
+        // ---------------- values, 16 tokens per pass.  Lane 16 q + 4 blk + m
+        // holds dims of block blk of token 4 q + m; a 4x4x4 MFMA against the
+        // identity transposes each 4-dim group within the quad of lanes
+        // (lane 4 b + n <- dim n of the quad's 4 tokens, exact), and a second
+        // one multiplies by the quad's weights.
 #pragma unroll
         for (int hp = 0; hp < kPasses; ++hp) {
-            {
-                uint32_t o[16];
-                if constexpr (pair_table<VB>()) {
+            uint32_t o[16];
+            if constexpr (pair_table<VB>()) {
 #pragma unroll
-                    for (int p = 0; p < 16; ++p)
-                        o[p] = *reinterpret_cast<const uint32_t *>(tab_bytes + kKTab + pair_offset(r.vw[hp], p, lane_off));
-                } else {
-                    unpack_block<VB>(vlut, r.vw[hp], o);
-                }
-                uint8_t * dst = vtile + vrow_off(lane & 15) + (lane >> 4) * 64;
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    *reinterpret_cast<u32x4 *>(dst + c * 16) = u32x4{o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]};
+                for (int p = 0; p < 16; ++p)
+                    o[p] = *reinterpret_cast<const uint32_t *>(tab_bytes + kKTab + pair_offset(r.vw[hp], p, lane_off));
+            } else {
+                unpack_block<VB>(vlut, r.vw[hp], o);
             }
+            const half4 aw = tr_read4(ptile, kPass * hp * 8 + p_off);
 #pragma unroll
-            for (int kk = 0; kk < kPass / 4; ++kk) {
-                const half4 aw = tr_read4(ptile, (kPass * hp + 4 * kk) * 8 + p_off);
-                // band rows 4kk..4kk+3: bit 2 of the row is kk & 1
-                const int band = 4 * kk * kVRow + (kk & 1) * 16;
-#pragma unroll
-                for (int dh = 0; dh < 2; ++dh) {
-                    const half4 bv = tr_read4(vtile, v_off + band + 128 * dh);
-                    acc[dh] = __builtin_amdgcn_mfma_f32_4x4x4f16(aw, bv, acc[dh], 0, 0, 0);
-                }
+            for (int gd = 0; gd < 8; ++gd) {
+                const floatx4 t = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(o[2 * gd], o[2 * gd + 1]), ident,
+                                                                     floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                acc[gd] = __builtin_amdgcn_mfma_f32_4x4x4f16(aw, to_half4(t), acc[gd], 0, 0, 0);
             }
         }
     };
@@ -515,13 +520,25 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
 #pragma unroll
     for (int h = 0; h < kG; ++h) lsum[h] = wave_sum(lsum[h]);
     __syncthreads();
+    // sum the four token quads (lanes 16 q + j), then lanes j < 16 hold
+    // block (j >> 2) & 3, dims 4 gd + (j & 3) of it
+#pragma unroll
+    for (int gd = 0; gd < 8; ++gd)
+#pragma unroll
+        for (int h = 0; h < kG; ++h) {
+            float v = acc[gd][h];
+            v += lane_xor<16>(v);
+            v += __shfl_xor(v, 32);
+            acc[gd][h] = v;
+        }
     float * res = reinterpret_cast<float *>(lds + wave * kWaveLds);  // [kG][kD + 2]
+    if (lane < 16) {
 #pragma unroll
-    for (int dh = 0; dh < 2; ++dh) {
-        const int c = 64 * dh + 4 * (lane >> 2) + (lane & 3);  // V tile column -> rotated-domain dim
-        const int dim = 32 * (c >> 5) + decoded_code_of_pos<VB>(c & 31);
+        for (int gd = 0; gd < 8; ++gd) {
+            const int dim = 32 * ((lane >> 2) & 3) + decoded_code_of_pos<VB>(4 * gd + (lane & 3));
 #pragma unroll
-        for (int h = 0; h < kG; ++h) res[h * (kD + 2) + 2 + dim] = acc[dh][h];
+            for (int h = 0; h < kG; ++h) res[h * (kD + 2) + 2 + dim] = acc[gd][h];
+        }
     }
     if (lane < kG) {
         res[lane * (kD + 2)] = mref[lane];
