@@ -140,17 +140,19 @@ __device__ __forceinline__ void buf_dwords(__amdgpu_buffer_rsrc_t r, uint32_t vo
     }
 }
 
-// 3-bit codes (keys and values alike) are decoded through a 64-entry LDS
-// table indexed by two consecutive codes (6 bits of the row's bit stream):
-// entry e holds the fp16 centroids of codes e & 7 and e >> 3.  The table is
-// stored 32 times, copy c in bank c (entry e of copy c at byte 128 e + 4 c),
-// and lane l reads copy l % 32, so the 32 lanes served together never share a
-// bank whatever codes they hold.  A lookup costs a shift, a mask-or and one
-// ds_read_b32 per two codes, and yields the pair in code order.
+// 3- and 4-bit codes (keys and values alike) are decoded through an LDS
+// table indexed by two consecutive codes (2 BITS bits of the row's bit
+// stream): entry e holds the fp16 centroids of codes e & (2^BITS - 1) and
+// e >> BITS.  The table is stored 32 times, copy c in bank c (entry e of copy
+// c at byte 128 e + 4 c), and lane l reads copy l % 32, so the 32 lanes served
+// together never share a bank whatever codes they hold.  A lookup costs a
+// shift, a mask-or and one ds_read_b32 per two codes, and yields the pair in
+// code order.  Sizes: 8 KB (3 bits), 32 KB (4 bits).
 template <int BITS>
-constexpr bool pair_table() { return BITS == 3; }
+constexpr bool pair_table() { return BITS == 3 || BITS == 4; }
 constexpr int kPairCopies = 32;
-constexpr int kPairTabBytes = 64 * kPairCopies * 4;
+template <int BITS>
+constexpr int pair_tab_bytes() { return pair_table<BITS>() ? (1 << (2 * BITS)) * kPairCopies * 4 : 0; }
 
 // Code index inside a 32-code block of output half `pos` as the decoder lays
 // the block out: pair-table look-ups keep code order, byte-permute unpacking
@@ -162,16 +164,18 @@ __host__ __device__ constexpr int decoded_code_of_pos(int pos) {
 
 // LDS byte offset of pair p (codes 2p, 2p+1) of the code row held in w, in
 // the copy whose offset is lane_off.
+template <int BITS>
 __device__ __forceinline__ uint32_t pair_offset(const uint32_t * w, int p, uint32_t lane_off) {
-    const int s = 6 * p, wi = s >> 5, o = s & 31;
+    constexpr int P = 2 * BITS;
+    const int s = P * p, wi = s >> 5, o = s & 31;
     uint32_t t;
-    if (o > 26)
+    if (o > 32 - P)
         t = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], o - 7);
     else if (o >= 7)
         t = w[wi] >> (o - 7);
     else
         t = w[wi] << (7 - o);
-    return (t & (63u << 7)) | lane_off;
+    return (t & (((1u << P) - 1) << 7)) | lane_off;
 }
 
 template <int KB, int VB, bool QJL>
@@ -200,8 +204,8 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     // one LDS array: the key pair table (if any) at offset 0, so that its
     // lookups need no base add, the value pair table (if any) at a constant
     // offset folded into the reads, then the four waves' tiles
-    constexpr int kKTab = pair_table<KB>() ? kPairTabBytes : 0;
-    constexpr int kVTab = pair_table<VB>() ? kPairTabBytes : 0;
+    constexpr int kKTab = pair_tab_bytes<KB>();
+    constexpr int kVTab = pair_tab_bytes<VB>();
     __shared__ __align__(16) uint8_t lds_all[kKTab + kVTab + 4 * kWaveLds];
     uint8_t * const lds = lds_all + kKTab + kVTab;
     uint32_t * const tabs = reinterpret_cast<uint32_t *>(lds_all);
@@ -270,15 +274,18 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     regs r0, r1;
     load_step(w_begin, r0);
 
-    // pair tables: thread t writes copy t % 32 of entries t / 32 + 8 k, i.e.
-    // low half cb[t / 32], high half cb[k]
-    auto fill_pair_table = [&](const dev_tables & tb, uint32_t * tab) {
-        const uint32_t lo = f16_bits(tb.cb[tid >> 5]);
+    // pair tables: thread t writes copies 4 (t % 8) .. + 3 of entries
+    // t / 8 + 32 k with one 16-byte store
+    auto fill_pair_table = [&](const dev_tables & tb, uint32_t * tab, auto bits_c) {
+        constexpr int B = decltype(bits_c)::value, E = 1 << (2 * B), M = (1 << B) - 1;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) tab[tid + 256 * k] = lo | (uint32_t(f16_bits(tb.cb[k])) << 16);
+        for (int e = tid >> 3; e < E; e += 32) {
+            const uint32_t v = uint32_t(f16_bits(tb.cb[e & M])) | (uint32_t(f16_bits(tb.cb[e >> B])) << 16);
+            *reinterpret_cast<u32x4 *>(tab + e * kPairCopies + 4 * (tid & 7)) = u32x4{v, v, v, v};
+        }
     };
-    if constexpr (pair_table<KB>()) fill_pair_table(kt, tabs);
-    if constexpr (pair_table<VB>()) fill_pair_table(vt, tabs + kKTab / 4);
+    if constexpr (pair_table<KB>()) fill_pair_table(kt, tabs, std::integral_constant<int, KB>{});
+    if constexpr (pair_table<VB>()) fill_pair_table(vt, tabs + kKTab / 4, std::integral_constant<int, VB>{});
 
     // ---- rotated queries.  MSE-only keys: each wave rotates its 4 heads
     // itself (q' = D1 H D2 q / sqrt(d), [TQ+ guide] §5.3): lane l holds
@@ -401,8 +408,8 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
             const uint8_t * tab = tab_bytes;
 #pragma unroll
             for (int gs = 0; gs < 32; ++gs) {
-                const uint32_t lo = *reinterpret_cast<const uint32_t *>(tab + pair_offset(r.kw, 2 * gs, lane_off));
-                const uint32_t hi = *reinterpret_cast<const uint32_t *>(tab + pair_offset(r.kw, 2 * gs + 1, lane_off));
+                const uint32_t lo = *reinterpret_cast<const uint32_t *>(tab + pair_offset<KB>(r.kw, 2 * gs, lane_off));
+                const uint32_t hi = *reinterpret_cast<const uint32_t *>(tab + pair_offset<KB>(r.kw, 2 * gs + 1, lane_off));
                 const half4 bk = as_half4(lo, hi);
                 Sc[2 * (gs & 1)] = mfma4_bcast(gs & 15, aq[gs >> 4][0], bk, Sc[2 * (gs & 1)]);
                 Sc[2 * (gs & 1) + 1] = mfma4_bcast(gs & 15, aq[gs >> 4][1], bk, Sc[2 * (gs & 1) + 1]);
@@ -482,7 +489,7 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
             if constexpr (pair_table<VB>()) {
 #pragma unroll
                 for (int p = 0; p < 16; ++p)
-                    o[p] = *reinterpret_cast<const uint32_t *>(tab_bytes + kKTab + pair_offset(r.vw[hp], p, lane_off));
+                    o[p] = *reinterpret_cast<const uint32_t *>(tab_bytes + kKTab + pair_offset<VB>(r.vw[hp], p, lane_off));
             } else {
                 unpack_block<VB>(vlut, r.vw[hp], o);
             }
