@@ -375,7 +375,9 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     const lut16 vlut = make_lut(vt.cb);
     const uint32_t lane_off = uint32_t(lane & 31) * 4;  // pair-table copy of this lane
     const float inv_sqrt_d = 1.0f / sqrtf(float(kD));
-    const float kscale = a.scale * inv_sqrt_d;
+    // logits are kept in base-2 units (scaled by log2 e), so weights are plain
+    // exp2; the reference is converted back to natural units at the end
+    const float kscale = a.scale * inv_sqrt_d * float(M_LOG2E);
     const float qjl_gain = sqrtf(0.5f * float(M_PI)) / float(kD) * sqrtf(float(kD));
     const float w_cap = __expf(kSlack);
 
@@ -455,20 +457,20 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
 #pragma unroll
         for (int h = 0; h < kG; ++h) {
             s[h] = own ? S[h] * ks_tok : -INFINITY;
-            p[h] = __expf(s[h] - mref[h]);
+            p[h] = __builtin_amdgcn_exp2f(s[h] - mref[h]);
             over |= !(p[h] * nv <= w_cap);  // also catches inf * 0 before the first max
         }
         if (__any(over)) {
-            const float lam = __logf(fmaxf(nv, 1e-26f));
+            const float lam = __builtin_amdgcn_logf(fmaxf(nv, 1e-26f));  // log2
 #pragma unroll
             for (int h = 0; h < kG; ++h) {
                 const float mn = fmaxf(mref[h], wave_max_uniform(s[h] + lam));
-                const float alpha = mref[h] == -INFINITY ? 0.f : __expf(mref[h] - mn);
+                const float alpha = mref[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref[h] - mn);
                 mref[h] = mn;
                 lsum[h] *= alpha;
 #pragma unroll
                 for (int gd = 0; gd < 8; ++gd) acc[gd][h] *= alpha;
-                p[h] = __expf(s[h] - mn);
+                p[h] = __builtin_amdgcn_exp2f(s[h] - mn);
             }
         }
 #pragma unroll
@@ -547,7 +549,7 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
         }
     }
     if (lane < kG) {
-        res[lane * (kD + 2)] = mref[lane];
+        res[lane * (kD + 2)] = mref[lane] * float(M_LN2);
         res[lane * (kD + 2) + 1] = lsum[lane];
     }
     __syncthreads();

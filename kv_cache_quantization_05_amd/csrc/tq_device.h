@@ -55,24 +55,25 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// Maximum over the wave, returned wave-uniform: DPP max within each row of 16
-// lanes (quad swaps, then half-row and row mirrors), then the four row results
-// read into scalars.
+// Maximum over the wave, returned wave-uniform.  Floats are mapped to
+// integers of the same order (negative values get their magnitude bits
+// flipped), so the row reductions are plain integer DPP maxima (quad swaps,
+// then half-row and row mirrors); the four row results are combined in
+// scalars.
+__device__ __forceinline__ int float_order_key(int b) { return b ^ ((b >> 31) & 0x7FFFFFFF); }
+
 __device__ __forceinline__ float wave_max_uniform(float v) {
-    auto dpp_max = [](float x, auto ctrl) {
-        const int y = __builtin_amdgcn_mov_dpp(__float_as_int(x), decltype(ctrl)::value, 0xF, 0xF, false);
-        return fmaxf(x, __int_as_float(y));
+    auto dpp_max = [](int x, auto ctrl) {
+        return max(x, __builtin_amdgcn_update_dpp(x, x, decltype(ctrl)::value, 0xF, 0xF, true));
     };
-    v = dpp_max(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
-    v = dpp_max(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
-    v = dpp_max(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
-    v = dpp_max(v, std::integral_constant<int, 0x140>{});  // row_mirror
-    const int b = __float_as_int(v);
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
-    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+    int k = float_order_key(__float_as_int(v));
+    k = dpp_max(k, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+    k = dpp_max(k, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+    k = dpp_max(k, std::integral_constant<int, 0x141>{});  // row_half_mirror
+    k = dpp_max(k, std::integral_constant<int, 0x140>{});  // row_mirror
+    const int m = max(max(__builtin_amdgcn_readlane(k, 0), __builtin_amdgcn_readlane(k, 16)),
+                      max(__builtin_amdgcn_readlane(k, 32), __builtin_amdgcn_readlane(k, 48)));
+    return __int_as_float(float_order_key(m));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
