@@ -309,8 +309,16 @@ __global__ __launch_bounds__(64) void scores_mfma_kernel(const dev_tables t, con
     __shared__ int32_t lst_i[TOPK ? 16 : 1][64];
     const int lane = threadIdx.x;
     const int n16 = lane & 15, g = lane >> 4;
-    const int64_t q0 = int64_t(blockIdx.x) * 16;
-    const int64_t k_begin = int64_t(blockIdx.y) * a.keys_per_range;
+    // XCD-aware order: blocks are dealt to the 8 XCDs round-robin, so block b
+    // takes work item (b % 8) * (grid / 8) + b / 8, and the query tiles of one
+    // key range run on one XCD and share its L2 (the grid is padded to a
+    // multiple of 8; padding blocks exit)
+    const int64_t n_qt = (a.n_q + 15) / 16;
+    const int64_t item = int64_t(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+    if (item >= n_qt * a.n_ranges) return;
+    const int64_t range = item / n_qt;
+    const int64_t q0 = (item % n_qt) * 16;
+    const int64_t k_begin = range * a.keys_per_range;
     const int64_t k_end = k_begin + a.keys_per_range < a.n_k ? k_begin + a.keys_per_range : a.n_k;
 
     // A operands: query n16, values of the k-step order of the B operand
@@ -416,7 +424,7 @@ __global__ __launch_bounds__(64) void scores_mfma_kernel(const dev_tables t, con
         for (int qi = 0; qi < 16; ++qi) {
             const int64_t q = q0 + qi;
             if (q < a.n_q && lane < K) {
-                const int64_t o = (int64_t(blockIdx.y) * a.n_q + q) * K + lane;
+                const int64_t o = (range * a.n_q + q) * K + lane;
                 a.cand_s[o] = lst_s[qi][lane];
                 a.cand_i[o] = lst_i[qi][lane] == INT32_MAX ? INT64_MAX : int64_t(lst_i[qi][lane]);
             }
@@ -427,7 +435,8 @@ __global__ __launch_bounds__(64) void scores_mfma_kernel(const dev_tables t, con
 template <int D, int KB, bool QJL>
 hipError_t launch_scores_t(const dev_tables & t, const scores_args & a, hipStream_t s) {
     if constexpr (D >= 128) {
-        const dim3 grid((a.n_q + 15) / 16, a.n_ranges);
+        const int64_t items = (a.n_q + 15) / 16 * a.n_ranges;
+        const dim3 grid(static_cast<uint32_t>((items + 7) / 8 * 8));
         if (a.top_k == 0) {
             hipLaunchKernelGGL((scores_mfma_kernel<D, KB, QJL, false>), grid, dim3(64), 0, s, t, a);
             return hipGetLastError();
