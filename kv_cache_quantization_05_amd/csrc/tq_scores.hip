@@ -352,24 +352,36 @@ __global__ __launch_bounds__(64) void scores_mfma_kernel(const dev_tables t, con
         __builtin_amdgcn_wave_barrier();
     }
 
-    for (int64_t j0 = k_begin; j0 < k_end; j0 += 16) {
+    // the next 16 keys' codes, signs and norms are loaded while the current
+    // ones are scored
+    uint32_t wn[NBL * KB], swn[NBL];
+    uint16_t nkn = 0, rkn = 0;
+    auto load_keys = [&](int64_t j0) {
         const int64_t key = j0 + n16;
-        const bool valid = key < k_end;
-        const int64_t kv = (valid ? key : k_end - 1) * a.k.stride[2];
-        uint32_t w[NBL * KB];
-        {
-            const uint32_t * crow = reinterpret_cast<const uint32_t *>(a.k.codes + kv * (D * KB / 8)) + NBL * KB * g;
+        const int64_t kv = (key < k_end ? key : k_end - 1) * a.k.stride[2];
+        const uint32_t * crow = reinterpret_cast<const uint32_t *>(a.k.codes + kv * (D * KB / 8)) + NBL * KB * g;
 #pragma unroll
-            for (int i = 0; i < NBL * KB; ++i) w[i] = crow[i];
-        }
-        uint32_t sw[NBL];
+        for (int i = 0; i < NBL * KB; ++i) wn[i] = crow[i];
         if constexpr (QJL) {
             const uint32_t * srow = reinterpret_cast<const uint32_t *>(a.k.signs + kv * (D / 8)) + NBL * g;
 #pragma unroll
-            for (int i = 0; i < NBL; ++i) sw[i] = srow[i];
+            for (int i = 0; i < NBL; ++i) swn[i] = srow[i];
+            rkn = a.k.rnorms[kv];
         }
-        const float nk = half_bits_to_float(a.k.norms[kv]);
-        const float gam = QJL ? half_bits_to_float(a.k.rnorms[kv]) * qjl_gain : 0.f;
+        nkn = a.k.norms[kv];
+    };
+    if (k_begin < k_end) load_keys(k_begin);
+    for (int64_t j0 = k_begin; j0 < k_end; j0 += 16) {
+        const int64_t key = j0 + n16;
+        const bool valid = key < k_end;
+        uint32_t w[NBL * KB], sw[NBL];
+#pragma unroll
+        for (int i = 0; i < NBL * KB; ++i) w[i] = wn[i];
+#pragma unroll
+        for (int i = 0; i < NBL; ++i) sw[i] = QJL ? swn[i] : 0u;
+        const float nk = half_bits_to_float(nkn);
+        const float gam = QJL ? half_bits_to_float(rkn) * qjl_gain : 0.f;
+        if (j0 + 16 < k_end) load_keys(j0 + 16);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f}, accq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int b = 0; b < NBL; ++b) {
