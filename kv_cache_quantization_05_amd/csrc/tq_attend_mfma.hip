@@ -140,44 +140,6 @@ __device__ __forceinline__ void buf_dwords(__amdgpu_buffer_rsrc_t r, uint32_t vo
     }
 }
 
-// 3- and 4-bit codes (keys and values alike) are decoded through an LDS
-// table indexed by two consecutive codes (2 BITS bits of the row's bit
-// stream): entry e holds the fp16 centroids of codes e & (2^BITS - 1) and
-// e >> BITS.  The table is stored 32 times, copy c in bank c (entry e of copy
-// c at byte 128 e + 4 c), and lane l reads copy l % 32, so the 32 lanes served
-// together never share a bank whatever codes they hold.  A lookup costs a
-// shift, a mask-or and one ds_read_b32 per two codes, and yields the pair in
-// code order.  Sizes: 8 KB (3 bits), 32 KB (4 bits).
-template <int BITS>
-constexpr bool pair_table() { return BITS == 3 || BITS == 4; }
-constexpr int kPairCopies = 32;
-template <int BITS>
-constexpr int pair_tab_bytes() { return pair_table<BITS>() ? (1 << (2 * BITS)) * kPairCopies * 4 : 0; }
-
-// Code index inside a 32-code block of output half `pos` as the decoder lays
-// the block out: pair-table look-ups keep code order, byte-permute unpacking
-// permutes it.
-template <int BITS>
-__host__ __device__ constexpr int decoded_code_of_pos(int pos) {
-    return pair_table<BITS>() ? pos : block_code_of_pos<BITS>(pos);
-}
-
-// LDS byte offset of pair p (codes 2p, 2p+1) of the code row held in w, in
-// the copy whose offset is lane_off.
-template <int BITS>
-__device__ __forceinline__ uint32_t pair_offset(const uint32_t * w, int p, uint32_t lane_off) {
-    constexpr int P = 2 * BITS;
-    const int s = P * p, wi = s >> 5, o = s & 31;
-    uint32_t t;
-    if (o > 32 - P)
-        t = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], o - 7);
-    else if (o >= 7)
-        t = w[wi] >> (o - 7);
-    else
-        t = w[wi] << (7 - o);
-    return (t & (((1u << P) - 1) << 7)) | lane_off;
-}
-
 template <int KB, int VB, bool QJL>
 struct step_regs {
     uint32_t kw[4 * KB];     // K code row of token lane (4 blocks)

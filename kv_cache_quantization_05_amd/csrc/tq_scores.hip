@@ -301,24 +301,39 @@ __device__ __forceinline__ void wave_insert(float * ls, int32_t * li, int K, flo
     __builtin_amdgcn_wave_barrier();
 }
 
+// Four waves per block, one 16-query tile each, over the same key range: the
+// key codes are fetched once into L1 for the four, and the 3/4-bit codes go
+// through one shared LDS pair table.
 template <int D, int KB, bool QJL, bool TOPK>
-__global__ __launch_bounds__(64) void scores_mfma_kernel(const dev_tables t, const scores_args a) {
+__global__ __launch_bounds__(256) void scores_mfma_kernel(const dev_tables t, const scores_args a) {
     constexpr int NBL = D / 128;  // code blocks per lane group
     constexpr int KS = 4 * NBL;   // k-steps (8 values per lane each)
-    __shared__ float lst_s[TOPK ? 16 : 1][64];
-    __shared__ int32_t lst_i[TOPK ? 16 : 1][64];
-    const int lane = threadIdx.x;
+    constexpr int kTab = pair_tab_bytes<KB>();
+    __shared__ __align__(16) uint32_t tab[kTab > 0 ? kTab / 4 : 1];
+    __shared__ float lst_s[4][TOPK ? 16 : 1][64];
+    __shared__ int32_t lst_i[4][TOPK ? 16 : 1][64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g = lane >> 4;
     // XCD-aware order: blocks are dealt to the 8 XCDs round-robin, so block b
     // takes work item (b % 8) * (grid / 8) + b / 8, and the query tiles of one
     // key range run on one XCD and share its L2 (the grid is padded to a
     // multiple of 8; padding blocks exit)
-    const int64_t n_qt = (a.n_q + 15) / 16;
+    const int64_t n_qt4 = ((a.n_q + 15) / 16 + 3) / 4;
     const int64_t item = int64_t(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
-    if (item >= n_qt * a.n_ranges) return;
-    const int64_t range = item / n_qt;
-    const int64_t q0 = (item % n_qt) * 16;
+    if (item >= n_qt4 * a.n_ranges) return;
+    const int64_t range = item / n_qt4;
+    const int64_t q0 = ((item % n_qt4) * 4 + wave) * 16;
     const int64_t k_begin = range * a.keys_per_range;
+    if constexpr (pair_table<KB>()) {
+        constexpr int E = 1 << (2 * KB), M = (1 << KB) - 1;
+        for (int e = tid >> 3; e < E; e += 32) {
+            const uint32_t v = uint32_t(f16_bits(t.cb[e & M])) | (uint32_t(f16_bits(t.cb[e >> KB])) << 16);
+            *reinterpret_cast<uint4 *>(tab + e * kPairCopies + 4 * (tid & 7)) = uint4{v, v, v, v};
+        }
+        __syncthreads();
+    }
+    const uint32_t lane_off = uint32_t(lane & 31) * 4;
     const int64_t k_end = k_begin + a.keys_per_range < a.n_k ? k_begin + a.keys_per_range : a.n_k;
 
     // A operands: query n16, values of the k-step order of the B operand
@@ -331,7 +346,7 @@ __global__ __launch_bounds__(64) void scores_mfma_kernel(const dev_tables t, con
             const int bl = NBL * g + ks / 4;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x = qrow[32 * bl + block_code_of_pos<KB>(8 * (ks % 4) + e)];
+                const float x = qrow[32 * bl + decoded_code_of_pos<KB>(8 * (ks % 4) + e)];
                 const _Float16 hi = static_cast<_Float16>(x);
                 aqh[ks][e] = hi;
                 aql[ks][e] = static_cast<_Float16>(x - static_cast<float>(hi));
@@ -346,8 +361,8 @@ __global__ __launch_bounds__(64) void scores_mfma_kernel(const dev_tables t, con
     float thr[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     if constexpr (TOPK) {
         for (int qi = 0; qi < 16; ++qi) {
-            lst_s[qi][lane] = -INFINITY;
-            lst_i[qi][lane] = INT32_MAX;
+            lst_s[wave][qi][lane] = -INFINITY;
+            lst_i[wave][qi][lane] = INT32_MAX;
         }
         __builtin_amdgcn_wave_barrier();
     }
@@ -386,7 +401,14 @@ __global__ __launch_bounds__(64) void scores_mfma_kernel(const dev_tables t, con
 #pragma unroll
         for (int b = 0; b < NBL; ++b) {
             uint32_t o[16];
-            unpack_block<KB>(lut, w + KB * b, o);
+            if constexpr (pair_table<KB>()) {
+#pragma unroll
+                for (int p = 0; p < 16; ++p)
+                    o[p] = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(tab) +
+                                                               pair_offset<KB>(w + KB * b, p, lane_off));
+            } else {
+                unpack_block<KB>(lut, w + KB * b, o);
+            }
 #pragma unroll
             for (int kq = 0; kq < 4; ++kq) {
                 const half8 bk = as_half8(o + 4 * kq);
@@ -425,8 +447,8 @@ __global__ __launch_bounds__(64) void scores_mfma_kernel(const dev_tables t, con
                         const int qi = 4 * (src >> 4) + i;
                         const float sv = __shfl(sc[i], src);
                         const int32_t iv = static_cast<int32_t>(__shfl(static_cast<int32_t>(key), src));
-                        wave_insert(lst_s[qi], lst_i[qi], K, sv, iv, lane);
-                        if ((lane >> 4) == (src >> 4)) thr[i] = lst_s[qi][K - 1];
+                        wave_insert(lst_s[wave][qi], lst_i[wave][qi], K, sv, iv, lane);
+                        if ((lane >> 4) == (src >> 4)) thr[i] = lst_s[wave][qi][K - 1];
                     }
                 }
             }
@@ -437,8 +459,8 @@ __global__ __launch_bounds__(64) void scores_mfma_kernel(const dev_tables t, con
             const int64_t q = q0 + qi;
             if (q < a.n_q && lane < K) {
                 const int64_t o = (range * a.n_q + q) * K + lane;
-                a.cand_s[o] = lst_s[qi][lane];
-                a.cand_i[o] = lst_i[qi][lane] == INT32_MAX ? INT64_MAX : int64_t(lst_i[qi][lane]);
+                a.cand_s[o] = lst_s[wave][qi][lane];
+                a.cand_i[o] = lst_i[wave][qi][lane] == INT32_MAX ? INT64_MAX : int64_t(lst_i[wave][qi][lane]);
             }
         }
     }
@@ -447,13 +469,13 @@ __global__ __launch_bounds__(64) void scores_mfma_kernel(const dev_tables t, con
 template <int D, int KB, bool QJL>
 hipError_t launch_scores_t(const dev_tables & t, const scores_args & a, hipStream_t s) {
     if constexpr (D >= 128) {
-        const int64_t items = (a.n_q + 15) / 16 * a.n_ranges;
+        const int64_t items = ((a.n_q + 15) / 16 + 3) / 4 * a.n_ranges;
         const dim3 grid(static_cast<uint32_t>((items + 7) / 8 * 8));
         if (a.top_k == 0) {
-            hipLaunchKernelGGL((scores_mfma_kernel<D, KB, QJL, false>), grid, dim3(64), 0, s, t, a);
+            hipLaunchKernelGGL((scores_mfma_kernel<D, KB, QJL, false>), grid, dim3(256), 0, s, t, a);
             return hipGetLastError();
         }
-        hipLaunchKernelGGL((scores_mfma_kernel<D, KB, QJL, true>), grid, dim3(64), 0, s, t, a);
+        hipLaunchKernelGGL((scores_mfma_kernel<D, KB, QJL, true>), grid, dim3(256), 0, s, t, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(topk_merge_kernel, dim3(a.n_q), dim3(64), 0, s, a);
