@@ -130,6 +130,31 @@ def test_attend_matches_oracle(kb, vb, qjl, G, d):
     _say("max rel / abs", worst)
 
 
+@pytest.mark.parametrize("kb", [2, 3, 4])
+@pytest.mark.parametrize("vb", [2, 3, 4])
+@pytest.mark.parametrize("qjl", [False, True])
+def test_attend_matrix_core_bit_widths(kb, vb, qjl):
+    """Every (key bits, value bits, QJL) instantiation of the d = 128, GQA 4
+    matrix-core path: pair-table and byte-permute decoders, ragged lengths."""
+    _say("attend mfma", kb, vb, qjl)
+    d, B, Hkv, G, T = 128, 2, 2, 4, 1500
+    kc = oenc.Config(seed=5, head_dim=d, bits=kb, qjl=qjl)
+    vc = oenc.Config(seed=5, head_dim=d, bits=vb)
+    rng = np.random.default_rng(1000 + kb * 100 + vb * 10 + qjl)
+    k = rng.standard_normal((B, Hkv, T, d)) * 1.5
+    v = rng.standard_normal((B, Hkv, T, d))
+    q = rng.standard_normal((B, Hkv * G, d)).astype(np.float32)
+    kp, vp = _oracle_planes(k, kc), _oracle_planes(v, vc)
+    lens = np.array([T, 777], dtype=np.int32)
+    ref = odec.attend_decode(q.astype(np.float64), kp, vp, kc, vc, lens)
+    kctx = tq.Context(seed=5, head_dim=d, bits=kb, qjl=qjl)
+    vctx = tq.Context(seed=5, head_dim=d, bits=vb)
+    out = tq.attend_decode(kctx, vctx, torch.from_numpy(q).to(DEV), tq.PackedPlanes.from_numpy(kp),
+                           tq.PackedPlanes.from_numpy(vp), torch.from_numpy(lens).to(DEV))
+    torch.cuda.synchronize()
+    _say("max rel / abs", assert_attend_close(out.cpu().numpy().astype(np.float64), ref))
+
+
 def test_attend_zero_and_clamped_lengths():
     d, B, Hkv, G, T = 128, 4, 1, 4, 300
     kc = vc = oenc.Config(seed=0, head_dim=d, bits=3)
@@ -195,7 +220,8 @@ def test_attend_reuses_one_workspace():
         _say("workspace reuse", lens.tolist(), assert_attend_close(out.cpu().numpy().astype(np.float64), ref))
 
 
-@pytest.mark.parametrize("d,bits,qjl", [(128, 4, False), (128, 3, True), (256, 4, True), (32, 2, False)])
+@pytest.mark.parametrize("d,bits,qjl", [(128, 4, False), (128, 3, True), (256, 4, True), (32, 2, False),
+                                        (256, 3, False), (128, 2, True)])
 def test_scores_full_matrix_matches_oracle(d, bits, qjl):
     cfg = oenc.Config(seed=3, head_dim=d, bits=bits, qjl=qjl)
     rng = np.random.default_rng(d + bits)
