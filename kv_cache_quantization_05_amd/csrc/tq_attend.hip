@@ -1,4 +1,6 @@
 // Decode attention dispatch: query prep, partial kernels, merge.
+#include <atomic>
+
 #include "tq_internal.h"
 
 namespace tq {
@@ -12,6 +14,24 @@ TQ_DECLARE_DIM(128)
 TQ_DECLARE_DIM(256)
 #undef TQ_DECLARE_DIM
 
+// Compute units of the current device, queried once per device.
+int current_cu_count() {
+    static std::atomic<int> counts[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev >= 64) {
+        hipDeviceProp_t prop;
+        return hipGetDeviceProperties(&prop, dev) == hipSuccess ? prop.multiProcessorCount : 256;
+    }
+    int n = counts[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        hipDeviceProp_t prop;
+        n = hipGetDeviceProperties(&prop, dev) == hipSuccess ? prop.multiProcessorCount : 256;
+        counts[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 // Tokens per split-K chunk.  Each (batch, KV head, chunk) is one block; the
 // chunk is a multiple of 256 tokens chosen so that the number of blocks fills
 // whole rounds of the resident block slots (no half-empty last round),
@@ -19,14 +39,7 @@ TQ_DECLARE_DIM(256)
 int attend_chunk_tokens(const dev_tables & kt, const dev_tables & vt, int32_t B, int32_t Hq, int32_t Hkv,
                         int64_t t_max) {
     if (t_max <= 0 || B <= 0 || Hkv <= 0) return 256;
-    static int cu_count = 0;
-    if (cu_count == 0) {
-        int dev = 0;
-        hipDeviceProp_t prop;
-        cu_count = (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
-                       ? prop.multiProcessorCount
-                       : 256;
-    }
+    const int cu_count = current_cu_count();
     const bool mfma = attend_mfma_shape_ok(kt, vt, Hq, Hkv);
     const int64_t slots = int64_t(cu_count) * (mfma ? attend_mfma_blocks_per_cu(kt, vt) : 2);
     const int64_t base = int64_t(B) * Hkv;

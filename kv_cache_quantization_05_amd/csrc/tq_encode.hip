@@ -27,6 +27,8 @@
 //  * QJL ctx (encode_qjl_kernel): the rotation, codes and residual in
 //    double, so that the fp16 residual norm also rounds exactly as float64
 //    does; the sketch S r on matrix cores (fp16 hi/lo split, ~22 bits).
+#include <atomic>
+
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -716,15 +718,16 @@ hipError_t launch_encode_dtype(const dev_tables & t, const encode_args & a, uint
             // each taking the same number of 64-vector iterations, with the
             // next iteration's inputs prefetched.  Larger inputs: a fixed grid
             // striding over the vectors, loading at each iteration's start.
-            static int cap = 0;
-            if (cap == 0) {
-                int dev = 0, per_cu = 0;
-                hipDeviceProp_t prop;
-                const bool ok = hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess &&
-                                hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, encode_mfma_kernel<DM, BITS, true>,
-                                                                             256, 0) == hipSuccess;
-                cap = ok && per_cu > 0 ? prop.multiProcessorCount * per_cu : 256 * 4;
+            static std::atomic<int> per_cu_cache{0};  // same on every gfx950 device
+            int per_cu = per_cu_cache.load(std::memory_order_relaxed);
+            if (per_cu == 0) {
+                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, encode_mfma_kernel<DM, BITS, true>, 256, 0) !=
+                        hipSuccess ||
+                    per_cu <= 0)
+                    per_cu = 4;
+                per_cu_cache.store(per_cu, std::memory_order_relaxed);
             }
+            const int cap = current_cu_count() * per_cu;
             const int64_t need = (int64_t(nvec) + 63) / 64;
             const int64_t iters = (need + cap - 1) / cap;
             if (iters <= 4) {

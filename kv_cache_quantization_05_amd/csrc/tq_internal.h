@@ -71,6 +71,8 @@ bool attend_mfma_shape_ok(const dev_tables & kt, const dev_tables & vt, int32_t 
 int attend_mfma_blocks_per_cu(const dev_tables & kt, const dev_tables & vt);
 hipError_t launch_attend_mfma_partial(const dev_tables & kt, const dev_tables & vt, const attend_args & a,
                                       hipStream_t s);
+// Compute units of the current device (queried once per device).
+int current_cu_count();
 int attend_chunk_tokens(const dev_tables & kt, const dev_tables & vt, int32_t B, int32_t Hq, int32_t Hkv,
                         int64_t t_max);
 
