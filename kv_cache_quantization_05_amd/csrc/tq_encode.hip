@@ -312,22 +312,26 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(const dev_tables t, con
                                                          const grid_index gi, const uint32_t nvec) {
     constexpr int LPV = D / 32;
     constexpr int VPB = 256 / LPV;   // vectors per workgroup iteration
-    constexpr int NT = (1 << BITS) - 1;
+    constexpr uint32_t kHalf = 1u << (BITS - 1);
     constexpr int RS = D + 8;        // LDS row stride (halves): rows start 16 B apart in the banks
     constexpr int RT = D / 16;       // 16-row tiles of S (m = d)
     constexpr int KS = D / 32;       // 32-wide k-steps
     constexpr int CT = VPB / 16;     // 16-vector column tiles
     constexpr int CB = CT < 4 ? CT : 4;
     __shared__ __align__(16) uint16_t rl[2][VPB * RS];
+    __shared__ float cpos[8];  // positive centroids cb[2^(b-1) + k]
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int blk = tid % LPV;
     const int vl = tid / LPV;        // vector within the workgroup's batch
     const uint32_t d1w = t.d1[blk];
     const uint32_t d2w = t.d2[blk];
-    float th[NT];
+    // positive thresholds th[2^(b-1) + j]; the codebook is exactly symmetric
+    float pth[8];
 #pragma unroll
-    for (int k = 0; k < NT; ++k) th[k] = t.th[k];
+    for (int j = 0; j < 8; ++j) pth[j] = j < int(kHalf) - 1 ? t.th[kHalf + j] : 0.f;
+    if (tid < int(kHalf)) cpos[tid] = t.cb[kHalf + tid];
+    __syncthreads();
     const uint16_t * const s_hi = t.S16;
     const uint16_t * const s_lo = t.S16 + D * D;
 
@@ -354,7 +358,11 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(const dev_tables t, con
             if ((d2w >> e) & 1) x[e] = -x[e];
         lane_fwht(x);
         cross_lane_fwht<LPV>(x, blk);
-        // z = sqrt(d) R x / n = D1 y / n;  code = #{k : th_k < z}
+        // z = sqrt(d) R x / n = D1 y / n;  code = #{k : th_k < z}, decided on
+        // fp32(z) (it differs from the float64 decision only within an fp32
+        // ulp of a threshold) through the codebook's symmetry:
+        // code = 2^(b-1) + k for z > 0, 2^(b-1) - 1 - k for z <= 0, with
+        // k = #{positive thresholds < |z|}; the residual stays in float64
         const double inv_n = n > 0.0 ? 1.0 / n : 0.0;
         uint32_t w[BITS];
 #pragma unroll
@@ -365,13 +373,15 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(const dev_tables t, con
         for (int e = 0; e < 32; ++e) {
             double z = x[e] * inv_n;
             if ((d1w >> e) & 1) z = -z;
-            uint32_t c = 0;
-#pragma unroll
-            for (int k = 0; k < NT; ++k) c += (z > static_cast<double>(th[k])) ? 1u : 0u;
+            const float zf = static_cast<float>(z);
+            const uint32_t kk = count_below<BITS>(fabsf(zf), pth);
+            const bool zneg = !(zf > 0.f);  // z = 0 (zero vectors) counts no threshold: 2^(b-1) - 1
+            const uint32_t c = zneg ? kHalf - 1 - kk : kHalf + kk;
             const int bit = BITS * e;
             w[bit >> 5] |= c << (bit & 31);
             if ((bit & 31) + BITS > 32) w[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
-            const double r = z - static_cast<double>(t.cb[c]);
+            const double cm = static_cast<double>(cpos[kk]);
+            const double r = zneg ? z + cm : z - cm;
             gsq = fma(r, r, gsq);
             const float rf = valid ? static_cast<float>(r) : 0.f;
             const _Float16 h = static_cast<_Float16>(rf);

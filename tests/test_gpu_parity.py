@@ -58,11 +58,12 @@ def test_encode_matches_oracle(d, bits, qjl, dtype):
 
 @pytest.mark.parametrize("bits", [3, 4])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_encode_extreme_magnitudes(bits, dtype):
+@pytest.mark.parametrize("qjl", [False, True])
+def test_encode_extreme_magnitudes(bits, dtype, qjl):
     # vectors far outside fp32's comfortable range for a 128-point transform
     # (norms from ~1e-35 to ~1e35), including subnormal coordinates
-    _say("encode extreme", bits, dtype)
-    ctx = tq.Context(seed=11, head_dim=128, bits=bits)
+    _say("encode extreme", bits, dtype, qjl)
+    ctx = tq.Context(seed=11, head_dim=128, bits=bits, qjl=qjl)
     scales = [1e-35, 1e-20, 2.0 ** -61, 2.0 ** -59, 1.0, 2.0 ** 59, 2.0 ** 61, 1e20, 1e35]
     x = _x((len(scales), 40, 128), torch.float32, seed=99 + bits)
     x = x * torch.tensor(scales).view(-1, 1, 1)
