@@ -10,9 +10,13 @@
 //           the query operand is broadcast from one block (CBSZ/ABID), so each
 //           lane stores query values for only 2 of the 32 k-steps.  q' is split
 //           into fp16 hi + lo parts (two instructions), ~22 bits of precision.
-//   values  O[h, i] += sum_t w[h, t] c[code_ti]: k runs over 4 tokens, block b
-//           covers 4 dims; the dequantised V tile goes through LDS and comes
-//           back transposed with ds_read_b64_tr_b16, as do the weights.
+//   values  O[h, i] += sum_t w[h, t] c[code_ti]: k runs over 4 tokens.  A
+//           lane holds dims of one token, so each 4-dim group is first
+//           transposed within its quad of lanes by a 4x4x4 MFMA against the
+//           identity (exact), then multiplied by the quad's weights, which
+//           come back from LDS transposed with ds_read_b64_tr_b16.
+// 3- and 4-bit codes are decoded through two-code LDS tables, 2-bit codes
+// with byte permutes.
 // Query rotation once per head ([TQ+ guide] §5.3), online softmax
 // ([TQ explainer] §4.3), the output stays in the rotated domain until the
 // merge kernel rotates it back ([TQ+ guide] §6.1).
@@ -25,10 +29,10 @@
 // one past the wave's range gets empty resources, so it costs no memory
 // traffic).
 //
-// Softmax bookkeeping per wave: a wave-uniform reference m per head, raised
-// only when a weight w = exp(s - m) * N_v/sqrt(d) would exceed e^kSlack (so
-// most steps need no cross-lane max); w stays safe in fp16 whatever the
-// norms, and the row sum accumulates exp(s - m) in fp32.
+// Softmax bookkeeping per wave, in base-2 units: a wave-uniform reference m
+// per head, raised only when a weight w = 2^(s - m) * N_v/sqrt(d) would exceed
+// e^kSlack (so most steps need no cross-lane max); w stays safe in fp16
+// whatever the norms, and the row sum accumulates 2^(s - m) in fp32.
 #include <cmath>
 
 #include "tq_device.h"
