@@ -157,6 +157,14 @@ struct step_regs {
 // the common 3-bit MSE-only case, else the compiler's choice.  Throughput
 // barely depends on occupancy here (one wave per SIMD already reaches most of
 // it), so registers go to the pipelined step data and accumulators.
+// Register sets of step data (NS - 1 steps in flight).  Two suffice: with
+// 3 or 4 sets (2 waves per SIMD) the 128K layer measured the same, and a
+// loads-only copy of the kernel reaches ~5.9 TB/s either way.
+template <int KB, int VB, bool QJL>
+constexpr int step_sets() {
+    return 2;
+}
+
 template <int KB, int VB, bool QJL>
 constexpr int waves_per_simd() {
     return (!QJL && VB == 3 && KB <= 3) ? 3 : 1;
@@ -237,8 +245,12 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     };
 
     // the first step's codes are in flight while the queries and tables are set up
-    regs r0, r1;
-    load_step(w_begin, r0);
+    // NS register sets: the steps NS - 1 ahead are in flight while one is
+    // processed
+    constexpr int NS = step_sets<KB, VB, QJL>();
+    regs rs[NS];
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i) load_step(w_begin + i * kStep, rs[i]);
 
     // pair tables: thread t writes copies 4 (t % 8) .. + 3 of entries
     // t / 8 + 32 k with one 16-byte store
@@ -476,18 +488,20 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     // youngest finishing alone; a wave drops its issue priority by one level
     // per quarter of its range done, so lagging waves catch up.
     const int64_t span = w_end > w_begin ? w_end - w_begin : 1;
-    for (int64_t j0 = w_begin; j0 < w_end; j0 += 2 * kStep) {
+    for (int64_t j0 = w_begin; j0 < w_end; j0 += NS * kStep) {
         switch (static_cast<int>((j0 - w_begin) * 4 / span)) {
             case 0: __builtin_amdgcn_s_setprio(3); break;
             case 1: __builtin_amdgcn_s_setprio(2); break;
             case 2: __builtin_amdgcn_s_setprio(1); break;
             default: __builtin_amdgcn_s_setprio(0); break;
         }
-        load_step(j0 + kStep, r1);
-        process(j0, r0);
-        if (j0 + kStep >= w_end) break;
-        load_step(j0 + 2 * kStep, r0);
-        process(j0 + kStep, r1);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const int64_t jj = j0 + i * kStep;
+            if (i > 0 && jj >= w_end) break;
+            load_step(jj + (NS - 1) * kStep, rs[(i + NS - 1) % NS]);
+            process(jj, rs[i]);
+        }
     }
 
     // ---- wave results: m, l (summed over the token lanes), acc
