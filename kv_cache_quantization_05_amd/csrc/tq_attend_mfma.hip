@@ -55,7 +55,7 @@ constexpr int kG = 4;
 constexpr int kStep = 64;                  // tokens per wave iteration (one per lane)
 constexpr int kPass = 16;                  // tokens per V tile pass
 constexpr int kPasses = kStep / kPass;
-constexpr int kStage = kG * kD * 4;       // rotated queries (prologue) / wave results (epilogue)
+constexpr int kStage = kG * kD * 4;       // wave results (epilogue)
 constexpr int kPTile = kStep * 8;          // 64 tokens x 4 heads x fp16
 constexpr int kWaveLds = kStage + kPTile;
 static_assert(kG * (kD + 2) * 4 <= kWaveLds, "wave results fit the wave's LDS");
@@ -178,18 +178,23 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     // one LDS array: the key pair table (if any) at offset 0, so that its
     // lookups need no base add, the value pair table (if any) at a constant
     // offset folded into the reads, then the four waves' tiles
-    constexpr int kKTab = pair_tab_bytes<KB>();
-    constexpr int kVTab = pair_tab_bytes<VB>();
-    __shared__ __align__(16) uint8_t lds_all[kKTab + kVTab + 4 * kWaveLds];
-    uint8_t * const lds = lds_all + kKTab + kVTab;
-    uint32_t * const tabs = reinterpret_cast<uint32_t *>(lds_all);
+    // 4-bit tables (keys in the low half of each 256-byte entry, values in
+    // the high half) at offset 0, where a byte permute yields the whole
+    // address; then the 3-bit key and value tables
+    constexpr int kByte = (KB == 4 || VB == 4) ? kByteTabBytes : 0;
+    constexpr int kK3 = KB == 3 ? pair_tab_bytes<3>() : 0;
+    constexpr int kV3 = VB == 3 ? pair_tab_bytes<3>() : 0;
+    constexpr int kKOff = kByte, kVOff = kByte + kK3;  // 3-bit table offsets
+    constexpr int kQStage = kG * 2 * kD * 4;  // the block's rotated queries and S q'
+    __shared__ __align__(16) uint8_t lds_all[kByte + kK3 + kV3 + kQStage + 4 * kWaveLds];
+    float * const qst = reinterpret_cast<float *>(lds_all + kByte + kK3 + kV3);  // [kG][2 kD]
+    uint8_t * const lds = lds_all + kByte + kK3 + kV3 + kQStage;
     const uint8_t * const tab_bytes = lds_all;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int lane = tid & 63;
     const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    uint8_t * stage = lds + wave * kWaveLds;
-    uint8_t * ptile = stage + kStage;
+    uint8_t * ptile = lds + wave * kWaveLds + kStage;  // the wave's softmax weights
 
     int64_t L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
     L = L < 0 ? 0 : (L > a.t_max ? a.t_max : L);
@@ -254,26 +259,29 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
 
     // pair tables: thread t writes copies 4 (t % 8) .. + 3 of entries
     // t / 8 + 32 k with one 16-byte store
-    auto fill_pair_table = [&](const dev_tables & tb, uint32_t * tab, auto bits_c) {
+    // pair tables: thread t writes copies 4 (t % 8) .. + 3 of entries
+    // t / 8 + 32 k with one 16-byte store (entry stride 128 B for 3 bits,
+    // 256 B for 4 bits)
+    auto fill_pair_table = [&](const dev_tables & tb, int offset, auto bits_c) {
         constexpr int B = decltype(bits_c)::value, E = 1 << (2 * B), M = (1 << B) - 1;
+        constexpr int stride = B == 4 ? 256 : 128;
 #pragma unroll
         for (int e = tid >> 3; e < E; e += 32) {
             const uint32_t v = uint32_t(f16_bits(tb.cb[e & M])) | (uint32_t(f16_bits(tb.cb[e >> B])) << 16);
-            *reinterpret_cast<u32x4 *>(tab + e * kPairCopies + 4 * (tid & 7)) = u32x4{v, v, v, v};
+            *reinterpret_cast<u32x4 *>(lds_all + offset + e * stride + 16 * (tid & 7)) = u32x4{v, v, v, v};
         }
     };
-    if constexpr (pair_table<KB>()) fill_pair_table(kt, tabs, std::integral_constant<int, KB>{});
-    if constexpr (pair_table<VB>()) fill_pair_table(vt, tabs + kKTab / 4, std::integral_constant<int, VB>{});
+    if constexpr (KB == 4) fill_pair_table(kt, 0, std::integral_constant<int, 4>{});
+    if constexpr (VB == 4) fill_pair_table(vt, 128, std::integral_constant<int, 4>{});
+    if constexpr (KB == 3) fill_pair_table(kt, kKOff, std::integral_constant<int, 3>{});
+    if constexpr (VB == 3) fill_pair_table(vt, kVOff, std::integral_constant<int, 3>{});
 
-    // ---- rotated queries.  MSE-only keys: each wave rotates its 4 heads
-    // itself (q' = D1 H D2 q / sqrt(d), [TQ+ guide] §5.3): lane l holds
-    // coordinates 8(l%16)..+7 of head l/16; three butterfly stages run in
-    // registers, four across the 16 lanes of the head; q' is staged in the
-    // wave's (not yet used) V tile.  QJL keys read q' and S q' prepared by the
-    // query kernel.
-    const float * qsrc;
-    int64_t qstride;
-    if constexpr (!QJL) {
+    // ---- rotated queries, once per block: wave 0 rotates the block's 4 heads
+    // (q' = D1 H D2 q / sqrt(d), [TQ+ guide] §5.3): lane l holds coordinates
+    // 8(l%16)..+7 of head l/16; three butterfly stages run in registers, four
+    // across the 16 lanes of the head.  For QJL keys the four waves then form
+    // S q' (rows 32 w .. 32 w + 31, two lanes per row).
+    if (wave == 0) {
         const int h = lane >> 4, e0 = 8 * (lane & 15);
         const float4 * src = reinterpret_cast<const float4 *>(a.q + (int64_t(b) * a.Hq + g * kG + h) * kD + e0);
         const float4 u0 = src[0], u1 = src[1];
@@ -314,16 +322,34 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
         const float rs = 1.0f / sqrtf(float(kD));
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = ((s1 >> i) & 1) ? -v[i] * rs : v[i] * rs;
-        float4 * dst = reinterpret_cast<float4 *>(stage + (h * kD + e0) * 4);
+        float4 * dst = reinterpret_cast<float4 *>(qst + h * 2 * kD + e0);
         dst[0] = float4{v[0], v[1], v[2], v[3]};
         dst[1] = float4{v[4], v[5], v[6], v[7]};
-        qsrc = reinterpret_cast<const float *>(stage);
-        qstride = kD;
-    } else {
-        qsrc = a.qp + (int64_t(b) * a.Hq + g * kG) * a.qp_stride;
-        qstride = a.qp_stride;
     }
-    __syncthreads();  // q' staged (and the pair table, below, filled)
+    __syncthreads();  // q' staged (and the pair tables filled)
+    if constexpr (QJL) {
+        const int row = 32 * wave + (lane >> 1), half = lane & 1;
+        const float4 * srow = reinterpret_cast<const float4 *>(kt.S + int64_t(row) * kD + 64 * half);
+        float u[kG] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int c = 0; c < 16; ++c) {
+            const float4 sv = srow[c];
+#pragma unroll
+            for (int h = 0; h < kG; ++h) {
+                const float4 qv = *reinterpret_cast<const float4 *>(qst + h * 2 * kD + 64 * half + 4 * c);
+                u[h] = fmaf(sv.x, qv.x, fmaf(sv.y, qv.y, fmaf(sv.z, qv.z, fmaf(sv.w, qv.w, u[h]))));
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < kG; ++h) u[h] += lane_xor<1>(u[h]);
+        if (half == 0) {
+#pragma unroll
+            for (int h = 0; h < kG; ++h) qst[h * 2 * kD + kD + row] = u[h];
+        }
+        __syncthreads();
+    }
+    const float * const qsrc = qst;
+    constexpr int64_t qstride = 2 * kD;
 
     half4 aq[2][2], au[2];
     {
@@ -385,11 +411,16 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
         // k-steps) keep dependent MFMAs apart.
         floatx4 Sc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         if constexpr (pair_table<KB>()) {
-            const uint8_t * tab = tab_bytes;
+            auto klook = [&](int p) {
+                if constexpr (KB == 4)
+                    return *reinterpret_cast<const uint32_t *>(tab_bytes + byte_pair_offset(r.kw, p, lane_off));
+                else
+                    return *reinterpret_cast<const uint32_t *>(tab_bytes + kKOff + pair_offset<KB>(r.kw, p, lane_off));
+            };
 #pragma unroll
             for (int gs = 0; gs < 32; ++gs) {
-                const uint32_t lo = *reinterpret_cast<const uint32_t *>(tab + pair_offset<KB>(r.kw, 2 * gs, lane_off));
-                const uint32_t hi = *reinterpret_cast<const uint32_t *>(tab + pair_offset<KB>(r.kw, 2 * gs + 1, lane_off));
+                const uint32_t lo = klook(2 * gs);
+                const uint32_t hi = klook(2 * gs + 1);
                 const half4 bk = as_half4(lo, hi);
                 Sc[2 * (gs & 1)] = mfma4_bcast(gs & 15, aq[gs >> 4][0], bk, Sc[2 * (gs & 1)]);
                 Sc[2 * (gs & 1) + 1] = mfma4_bcast(gs & 15, aq[gs >> 4][1], bk, Sc[2 * (gs & 1) + 1]);
@@ -468,7 +499,8 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
             if constexpr (pair_table<VB>()) {
 #pragma unroll
                 for (int p = 0; p < 16; ++p)
-                    o[p] = *reinterpret_cast<const uint32_t *>(tab_bytes + kKTab + pair_offset<VB>(r.vw[hp], p, lane_off));
+                    o[p] = VB == 4 ? *reinterpret_cast<const uint32_t *>(tab_bytes + byte_pair_offset(r.vw[hp], p, lane_off | 128u))
+                                   : *reinterpret_cast<const uint32_t *>(tab_bytes + kVOff + pair_offset<VB>(r.vw[hp], p, lane_off));
             } else {
                 unpack_block<VB>(vlut, r.vw[hp], o);
             }

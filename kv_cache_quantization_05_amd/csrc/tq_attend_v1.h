@@ -344,8 +344,8 @@ hipError_t launch_attend_g(const dev_tables & kt, const dev_tables & vt, const a
                            hipStream_t s) {
     const dim3 grid(a.n_chunks, a.Hkv, a.B);
     const bool mfma = attend_mfma_supported(kt, vt, a);
-    // the matrix-core kernel rotates MSE-only queries itself
-    if (!mfma || kt.qjl) {
+    // the matrix-core kernel prepares its queries itself
+    if (!mfma) {
         hipError_t e = launch_query_prep(kt, a.q, int64_t(a.B) * a.Hq, a.qp, a.qp_stride, s);
         if (e != hipSuccess) return e;
     }

@@ -176,4 +176,14 @@ __device__ __forceinline__ uint32_t pair_offset(const uint32_t * w, int p, uint3
     return (t & (((1u << P) - 1) << 7)) | lane_off;
 }
 
+// 4-bit codes: the pair of codes 2p, 2p+1 is byte p of the row, so the LDS
+// address of its table entry comes from one byte permute: entry e sits at
+// byte 256 e, copy c of a key table at +4 c and of a value table at
+// +128 + 4 c (one 64 KB region serves both).  base_byte is the lane's copy
+// offset plus 128 for the value half (< 256).
+constexpr int kByteTabBytes = 256 * 256;
+__device__ __forceinline__ uint32_t byte_pair_offset(const uint32_t * w, int p, uint32_t base_byte) {
+    return __builtin_amdgcn_perm(w[p >> 2], base_byte, 0x0C0C0000u | ((4u + uint32_t(p & 3)) << 8));
+}
+
 }  // namespace tq
