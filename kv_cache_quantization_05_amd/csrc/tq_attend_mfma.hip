@@ -249,32 +249,51 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
         }
     };
 
-    // the first step's codes are in flight while the queries and tables are set up
-    // NS register sets: the steps NS - 1 ahead are in flight while one is
-    // processed
+    // The queries are loaded first: vector-memory waits are in order, so a
+    // load issued after the first step's codes would wait for them.  Then the
+    // codes are in flight while the queries and tables are set up (NS
+    // register sets: the steps NS - 1 ahead are in flight while one is
+    // processed).
+    float4 qv0 = {0.f, 0.f, 0.f, 0.f}, qv1 = {0.f, 0.f, 0.f, 0.f};
+    if (wave == 0) {
+        const float4 * src = reinterpret_cast<const float4 *>(a.q + (int64_t(b) * a.Hq + g * kG + (lane >> 4)) * kD +
+                                                              8 * (lane & 15));
+        qv0 = src[0];
+        qv1 = src[1];
+    }
+    // QJL keys: this lane's half row of S (row 32 w + lane / 2), for S q'
+    float4 srow[QJL ? 16 : 1];
+    if constexpr (QJL) {
+        const float4 * sp = reinterpret_cast<const float4 *>(kt.S + int64_t(32 * wave + (lane >> 1)) * kD + 64 * (lane & 1));
+#pragma unroll
+        for (int c = 0; c < 16; ++c) srow[c] = sp[c];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the codes
     constexpr int NS = step_sets<KB, VB, QJL>();
     regs rs[NS];
 #pragma unroll
     for (int i = 0; i < NS - 1; ++i) load_step(w_begin + i * kStep, rs[i]);
+    const lut16 klut = make_lut(kt.cb);
+    const lut16 vlut = make_lut(vt.cb);
 
-    // pair tables: thread t writes copies 4 (t % 8) .. + 3 of entries
-    // t / 8 + 32 k with one 16-byte store
     // pair tables: thread t writes copies 4 (t % 8) .. + 3 of entries
     // t / 8 + 32 k with one 16-byte store (entry stride 128 B for 3 bits,
     // 256 B for 4 bits)
-    auto fill_pair_table = [&](const dev_tables & tb, int offset, auto bits_c) {
+    // (centroid bits from the byte planes, not a per-lane kernel-argument
+    // index, which would be a vector load)
+    auto fill_pair_table = [&](const lut16 & tl, int offset, auto bits_c) {
         constexpr int B = decltype(bits_c)::value, E = 1 << (2 * B), M = (1 << B) - 1;
         constexpr int stride = B == 4 ? 256 : 128;
 #pragma unroll
         for (int e = tid >> 3; e < E; e += 32) {
-            const uint32_t v = uint32_t(f16_bits(tb.cb[e & M])) | (uint32_t(f16_bits(tb.cb[e >> B])) << 16);
+            const uint32_t v = lut_bits<B>(tl, uint32_t(e & M)) | (lut_bits<B>(tl, uint32_t(e >> B)) << 16);
             *reinterpret_cast<u32x4 *>(lds_all + offset + e * stride + 16 * (tid & 7)) = u32x4{v, v, v, v};
         }
     };
-    if constexpr (KB == 4) fill_pair_table(kt, 0, std::integral_constant<int, 4>{});
-    if constexpr (VB == 4) fill_pair_table(vt, 128, std::integral_constant<int, 4>{});
-    if constexpr (KB == 3) fill_pair_table(kt, kKOff, std::integral_constant<int, 3>{});
-    if constexpr (VB == 3) fill_pair_table(vt, kVOff, std::integral_constant<int, 3>{});
+    if constexpr (KB == 4) fill_pair_table(klut, 0, std::integral_constant<int, 4>{});
+    if constexpr (VB == 4) fill_pair_table(vlut, 128, std::integral_constant<int, 4>{});
+    if constexpr (KB == 3) fill_pair_table(klut, kKOff, std::integral_constant<int, 3>{});
+    if constexpr (VB == 3) fill_pair_table(vlut, kVOff, std::integral_constant<int, 3>{});
 
     // ---- rotated queries, once per block: wave 0 rotates the block's 4 heads
     // (q' = D1 H D2 q / sqrt(d), [TQ+ guide] §5.3): lane l holds coordinates
@@ -283,10 +302,14 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     // S q' (rows 32 w .. 32 w + 31, two lanes per row).
     if (wave == 0) {
         const int h = lane >> 4, e0 = 8 * (lane & 15);
-        const float4 * src = reinterpret_cast<const float4 *>(a.q + (int64_t(b) * a.Hq + g * kG + h) * kD + e0);
-        const float4 u0 = src[0], u1 = src[1];
-        float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-        const uint32_t s2 = kt.d2[e0 >> 5] >> (e0 & 31), s1 = kt.d1[e0 >> 5] >> (e0 & 31);
+        float v[8] = {qv0.x, qv0.y, qv0.z, qv0.w, qv1.x, qv1.y, qv1.z, qv1.w};
+        // sign words picked from the (uniform) four words by selects: a
+        // per-lane index into the kernel arguments would be a vector load,
+        // waiting behind the codes already in flight
+        const int wi = e0 >> 5;
+        const uint32_t d2w = wi == 0 ? kt.d2[0] : wi == 1 ? kt.d2[1] : wi == 2 ? kt.d2[2] : kt.d2[3];
+        const uint32_t d1w = wi == 0 ? kt.d1[0] : wi == 1 ? kt.d1[1] : wi == 2 ? kt.d1[2] : kt.d1[3];
+        const uint32_t s2 = d2w >> (e0 & 31), s1 = d1w >> (e0 & 31);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             if ((s2 >> i) & 1) v[i] = -v[i];
@@ -329,9 +352,8 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     __syncthreads();  // q' staged (and the pair tables filled)
     if constexpr (QJL) {
         const int row = 32 * wave + (lane >> 1), half = lane & 1;
-        const float4 * srow = reinterpret_cast<const float4 *>(kt.S + int64_t(row) * kD + 64 * half);
         float u[kG] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
+#pragma unroll
         for (int c = 0; c < 16; ++c) {
             const float4 sv = srow[c];
 #pragma unroll
@@ -375,8 +397,6 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
             }
         }
     }
-    const lut16 klut = make_lut(kt.cb);
-    const lut16 vlut = make_lut(vt.cb);
     const uint32_t lane_off = uint32_t(lane & 31) * 4;  // pair-table copy of this lane
     const float inv_sqrt_d = 1.0f / sqrtf(float(kD));
     // logits are kept in base-2 units (scaled by log2 e), so weights are plain
@@ -538,7 +558,7 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
 
     // ---- wave results: m, l (summed over the token lanes), acc
 #pragma unroll
-    for (int h = 0; h < kG; ++h) lsum[h] = wave_sum(lsum[h]);
+    for (int h = 0; h < kG; ++h) lsum[h] = wave_sum_dpp(lsum[h]);
     __syncthreads();
     // sum the four token quads (lanes 16 q + j), then lanes j < 16 hold
     // block (j >> 2) & 3, dims 4 gd + (j & 3) of it
@@ -546,10 +566,7 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     for (int gd = 0; gd < 8; ++gd)
 #pragma unroll
         for (int h = 0; h < kG; ++h) {
-            float v = acc[gd][h];
-            v += lane_xor<16>(v);
-            v += __shfl_xor(v, 32);
-            acc[gd][h] = v;
+            acc[gd][h] = add_xor16(add_xor32(acc[gd][h]));
         }
     float * res = reinterpret_cast<float *>(lds + wave * kWaveLds);  // [kG][kD + 2]
     if (lane < 16) {

@@ -76,6 +76,31 @@ __device__ __forceinline__ float wave_max_uniform(float v) {
     return __int_as_float(float_order_key(m));
 }
 
+// x + (the same register of lane l ^ 32) and of lane l ^ 16, with the
+// cross-row permlane swaps of gfx950 (no LDS traffic).
+__device__ __forceinline__ float add_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+    return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
+// Sum over the wave, in every lane: DPP adds within rows of 16, then the
+// two cross-row permlane swaps.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    auto dpp_add = [](float x, auto ctrl) {
+        return x + __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x),
+                                                              decltype(ctrl)::value, 0xF, 0xF, true));
+    };
+    v = dpp_add(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+    v = dpp_add(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+    v = dpp_add(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+    v = dpp_add(v, std::integral_constant<int, 0x140>{});  // row_mirror
+    return add_xor32(add_xor16(v));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
     return v;

@@ -72,6 +72,14 @@ __device__ __forceinline__ void lut4(const lut16 & t, uint32_t sel, uint32_t & x
     y = perm_b32(hi, lo, 0x07030602u);
 }
 
+// fp16 bits of centroid idx (< 2^BITS), from the byte planes.
+template <int BITS>
+__device__ __forceinline__ uint32_t lut_bits(const lut16 & t, uint32_t idx) {
+    uint32_t x, y;
+    lut4<BITS>(t, idx, x, y);
+    return x & 0xFFFFu;
+}
+
 // Code index inside the block of output half `pos` (0..31).
 template <int BITS>
 __host__ __device__ constexpr int block_code_of_pos(int pos) {
