@@ -221,6 +221,51 @@ def test_attend_reuses_one_workspace():
         _say("workspace reuse", lens.tolist(), assert_attend_close(out.cpu().numpy().astype(np.float64), ref))
 
 
+@pytest.mark.parametrize("kb,vb,qjl", [(3, 3, False), (4, 4, True)])
+def test_attend_long_context_counts_every_token_once(kb, vb, qjl):
+    """At long contexts each (batch, KV head) is split over many blocks and
+    waves.  Every cached token must be counted exactly once: with one key
+    repeated over the context (equal weights) and values +v for
+    the first half of each sequence and the mirrored codes for the second half
+    (-v: mirroring every b-bit code is a bitwise NOT of the packed bytes, and
+    the Lloyd-Max codebook of a symmetric density is symmetric), the exact
+    output is zero, while one 64-token step counted twice or skipped leaves
+    at least 64 |v| / L."""
+    d, B, Hkv, G, T = 128, 4, 8, 4, 32768
+    kctx = tq.Context(seed=3, head_dim=d, bits=kb, qjl=qjl)
+    vctx = tq.Context(seed=3, head_dim=d, bits=vb)
+    gen = torch.Generator().manual_seed(77)
+
+    def rand_bytes(n):
+        return torch.randint(0, 256, (B, Hkv, 1, n), generator=gen, dtype=torch.uint8)
+
+    kp = tq.PackedPlanes.empty(kctx, (B, Hkv, T), DEV)
+    kp.codes.copy_(rand_bytes(kctx.code_bytes).expand(B, Hkv, T, kctx.code_bytes))
+    kp.norms.fill_(0x3C00)                      # fp16 1.0
+    if qjl:
+        kp.signs.copy_(rand_bytes(kctx.sign_bytes).expand(B, Hkv, T, kctx.sign_bytes))
+        kp.rnorms.fill_(0x3400)                 # fp16 0.25
+    lens = [T, T - 2 * 4321, 2 * 6000, 2 * 777]  # even lengths
+    cv = rand_bytes(vctx.code_bytes)
+    codes = torch.full((B, Hkv, T, vctx.code_bytes), 0xFF, dtype=torch.uint8)
+    norms = torch.full((B, Hkv, T), -1, dtype=torch.int16)   # NaN fp16 past each length
+    for b, L in enumerate(lens):
+        codes[b, :, :L // 2] = cv[b]
+        codes[b, :, L // 2:L] = ~cv[b]
+        norms[b, :, :L] = 0x3C00
+    vp = tq.PackedPlanes.empty(vctx, (B, Hkv, T), DEV)
+    vp.codes.copy_(codes)
+    vp.norms.copy_(norms)
+    q = torch.randn((B, Hkv * G, d), generator=gen).to(DEV)
+    out = tq.attend_decode(kctx, vctx, q, kp, vp, torch.tensor(lens, dtype=torch.int32, device=DEV), t_max=T)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().astype(np.float64)
+    worst = float(np.abs(o).max())
+    _say("long-context token coverage", kb, vb, qjl, "max |out|", worst, "one step of the shortest:", 64 / min(lens))
+    assert np.all(np.isfinite(o))
+    assert worst <= 1e-4
+
+
 @pytest.mark.parametrize("d,bits,qjl", [(128, 4, False), (128, 3, True), (256, 4, True), (32, 2, False),
                                         (256, 3, False), (128, 2, True)])
 def test_scores_full_matrix_matches_oracle(d, bits, qjl):
