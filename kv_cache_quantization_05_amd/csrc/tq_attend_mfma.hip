@@ -1,22 +1,23 @@
 // Fused decode attention on matrix cores, d = 128, 4 query heads per KV head.
 //
 // The 4 grouped queries sharing one KV head form a real dense contraction
-// against the dequantised codes, so both products run on the 16-block 4x4x4
-// fp16 MFMA (v_mfma_f32_4x4x4_16b_f16), whose 4-row blocks match the 4 heads
-// exactly (no padded rows):
-//   logits  S[h, t] = sum_i q'[h, i] c[code_ti]: block b covers tokens
-//           4b..4b+3, so lane l ends up holding the 4 head logits of token l;
-//           k runs over 4 dims per instruction, 32 instructions per 128 dims;
-//           the query operand is broadcast from one block (CBSZ/ABID), so each
-//           lane stores query values for only 2 of the 32 k-steps.  q' is split
-//           into fp16 hi + lo parts (two instructions), ~22 bits of precision.
-//   values  O[h, i] += sum_t w[h, t] c[code_ti]: k runs over 4 tokens.  A
-//           lane holds dims of one token, so each 4-dim group is first
-//           transposed within its quad of lanes by a 4x4x4 MFMA against the
-//           identity (exact), then multiplied by the quad's weights, which
-//           come back from LDS transposed with ds_read_b64_tr_b16.
-// 3- and 4-bit codes are decoded through two-code LDS tables, 2-bit codes
-// with byte permutes.
+// against the dequantised codes, so both products run on matrix cores:
+//   logits  S[h, t] = sum_i q'[h, i] c[code_ti] on the 16x16x32 fp16 MFMA:
+//           columns are 16 tokens, rows the fp16 hi parts (rows 0..3) and lo
+//           parts (rows 4..7) of the 4 rotated queries (~22 bits of q'),
+//           rows 8..15 zero; lane l feeds 8 decoded values of code block
+//           l / 16 of token l % 16.  Two row swaps (permlane16/32) add the
+//           parts and leave lane l with the 4 head logits of token l.
+//   values  O[h, i] += sum_t w[h, t] c[code_ti] on the 16-block 4x4x4 fp16
+//           MFMA, whose 4-row blocks match the 4 heads exactly: k runs over
+//           4 tokens.  A lane holds dims of one token, so each 4-dim group
+//           is first transposed within its quad of lanes by a 4x4x4 MFMA
+//           against the identity (exact), then multiplied by the quad's
+//           weights, which come back from LDS transposed with
+//           ds_read_b64_tr_b16.
+// 3- and 4-bit codes are decoded two at a time through one 64 KB LDS table
+// indexed by a byte of the code row (a byte permute forms the whole
+// address); 2-bit codes with byte permutes in registers.
 // Query rotation once per head ([TQ+ guide] §5.3), online softmax
 // ([TQ explainer] §4.3), the output stays in the rotated domain until the
 // merge kernel rotates it back ([TQ+ guide] §6.1).
@@ -43,6 +44,7 @@ namespace tq {
 namespace {
 
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
@@ -76,6 +78,12 @@ __device__ __forceinline__ half4 to_half4(floatx4 c) {
     half4 h;
     __builtin_memcpy(&h, &lo, 4);
     __builtin_memcpy(reinterpret_cast<char *>(&h) + 4, &hi, 4);
+    return h;
+}
+
+__device__ __forceinline__ half8 as_half8(const uint32_t * w) {
+    half8 h;
+    __builtin_memcpy(&h, w, 16);
     return h;
 }
 
@@ -146,17 +154,18 @@ __device__ __forceinline__ void buf_dwords(__amdgpu_buffer_rsrc_t r, uint32_t vo
 
 template <int KB, int VB, bool QJL>
 struct step_regs {
-    uint32_t kw[4 * KB];     // K code row of token lane (4 blocks)
+    uint32_t kw[4 * KB];     // K code block lane/16 of tokens lane%16 + 16 tg, tg = 0..3
     uint32_t vw[kPasses][VB];  // V block (lane>>4) of token 16 pass + (lane&15)
     uint32_t ks[QJL ? 4 : 1];
     uint16_t kr;             // QJL residual norm
     uint16_t nk, nv;         // K and V norms of token lane
 };
 
-// Waves per SIMD the register budget is sized for: 3 (at most 168 VGPRs) for
-// the common 3-bit MSE-only case, else the compiler's choice.  Throughput
-// barely depends on occupancy here (one wave per SIMD already reaches most of
-// it), so registers go to the pipelined step data and accumulators.
+// Waves per SIMD the register budget is sized for: 2 (at most 256 VGPRs; two
+// blocks' 78 KB of LDS fill a compute unit) for the common 3-bit MSE-only
+// case, else the compiler's choice.  Throughput barely depends on occupancy
+// here (one wave per SIMD already reaches most of it), so registers go to the
+// pipelined step data and accumulators.
 // Register sets of step data (NS - 1 steps in flight).  Two suffice: with
 // 3 or 4 sets (2 waves per SIMD) the 128K layer measured the same, and a
 // loads-only copy of the kernel reaches ~5.9 TB/s either way.
@@ -167,7 +176,7 @@ constexpr int step_sets() {
 
 template <int KB, int VB, bool QJL>
 constexpr int waves_per_simd() {
-    return (!QJL && VB == 3 && KB <= 3) ? 3 : 1;
+    return (!QJL && VB == 3 && KB <= 3) ? 2 : 1;
 }
 
 template <int KB, int VB, bool QJL>
@@ -175,20 +184,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 256), amdgpu_waves_per_
 void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
                                                           const attend_args a) {
     constexpr uint32_t kKcb = kD * KB / 8, kVcb = kD * VB / 8;
-    // one LDS array: the key pair table (if any) at offset 0, so that its
-    // lookups need no base add, the value pair table (if any) at a constant
-    // offset folded into the reads, then the four waves' tiles
-    // 4-bit tables (keys in the low half of each 256-byte entry, values in
-    // the high half) at offset 0, where a byte permute yields the whole
-    // address; then the 3-bit key and value tables
-    constexpr int kByte = (KB == 4 || VB == 4) ? kByteTabBytes : 0;
-    constexpr int kK3 = KB == 3 ? pair_tab_bytes<3>() : 0;
-    constexpr int kV3 = VB == 3 ? pair_tab_bytes<3>() : 0;
-    constexpr int kKOff = kByte, kVOff = kByte + kK3;  // 3-bit table offsets
+    // one LDS array: the 3/4-bit byte tables (keys in the low half of each
+    // 256-byte entry, values in the high half) at offset 0, where a byte
+    // permute yields the whole address; then the block's queries and the
+    // four waves' tiles
+    constexpr int kByte = (pair_table<KB>() || pair_table<VB>()) ? kByteTabBytes : 0;
     constexpr int kQStage = kG * 2 * kD * 4;  // the block's rotated queries and S q'
-    __shared__ __align__(16) uint8_t lds_all[kByte + kK3 + kV3 + kQStage + 4 * kWaveLds];
-    float * const qst = reinterpret_cast<float *>(lds_all + kByte + kK3 + kV3);  // [kG][2 kD]
-    uint8_t * const lds = lds_all + kByte + kK3 + kV3 + kQStage;
+    __shared__ __align__(16) uint8_t lds_all[kByte + kQStage + 4 * kWaveLds];
+    float * const qst = reinterpret_cast<float *>(lds_all + kByte);  // [kG][2 kD]
+    uint8_t * const lds = lds_all + kByte + kQStage;
     const uint8_t * const tab_bytes = lds_all;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -223,7 +227,9 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     const uint8_t * const ks0 = QJL ? a.k.signs + kvec * (kD / 8) : nullptr;
     const uint16_t * const kr0 = QJL ? a.k.rnorms + kvec : nullptr;
     // per-lane byte offsets relative to the step's first token
-    const uint32_t vo_k = uint32_t(lane) * ks2 * kKcb;
+    uint32_t vo_k[4];
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) vo_k[tg] = uint32_t((lane & 15) + 16 * tg) * ks2 * kKcb + (lane >> 4) * 4 * KB;
     const uint32_t vo_kn = uint32_t(lane) * ks2 * 2;
     const uint32_t vo_ks = uint32_t(lane) * ks2 * (kD / 8);
     const uint32_t vo_vn = uint32_t(lane) * vs2 * 2;
@@ -237,7 +243,9 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
         const int64_t j = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(j0 < w_end ? j0 : L));  // wave-uniform
         const uint32_t left = static_cast<uint32_t>(L - j);  // tokens from j to L (0 past the end)
         const int64_t kj = j * ks2, vj = j * vs2;
-        buf_dwords<4 * KB>(make_rsrc(kc0 + kj * kKcb, left * ks2 * kKcb), vo_k, 0, r.kw);
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc0 + kj * kKcb, left * ks2 * kKcb);
+#pragma unroll
+        for (int tg = 0; tg < 4; ++tg) buf_dwords<KB>(rk, vo_k[tg], 0, r.kw + KB * tg);
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc0 + vj * kVcb, left * vs2 * kVcb);
 #pragma unroll
         for (int hp = 0; hp < kPasses; ++hp) buf_dwords<VB>(rv, vo_v[hp], 0, r.vw[hp]);
@@ -276,24 +284,21 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     const lut16 klut = make_lut(kt.cb);
     const lut16 vlut = make_lut(vt.cb);
 
-    // pair tables: thread t writes copies 4 (t % 8) .. + 3 of entries
-    // t / 8 + 32 k with one 16-byte store (entry stride 128 B for 3 bits,
-    // 256 B for 4 bits)
+    // byte tables: thread t writes copies 4 (t % 8) .. + 3 of entries
+    // t / 8 + 32 k with one 16-byte store; entry e holds the centroids of
+    // the codes in its low and high BITS bits (3-bit entries ignore bits 6, 7)
     // (centroid bits from the byte planes, not a per-lane kernel-argument
     // index, which would be a vector load)
-    auto fill_pair_table = [&](const lut16 & tl, int offset, auto bits_c) {
-        constexpr int B = decltype(bits_c)::value, E = 1 << (2 * B), M = (1 << B) - 1;
-        constexpr int stride = B == 4 ? 256 : 128;
+    auto fill_byte_table = [&](const lut16 & tl, int offset, auto bits_c) {
+        constexpr int B = decltype(bits_c)::value, M = (1 << B) - 1;
 #pragma unroll
-        for (int e = tid >> 3; e < E; e += 32) {
-            const uint32_t v = lut_bits<B>(tl, uint32_t(e & M)) | (lut_bits<B>(tl, uint32_t(e >> B)) << 16);
-            *reinterpret_cast<u32x4 *>(lds_all + offset + e * stride + 16 * (tid & 7)) = u32x4{v, v, v, v};
+        for (int e = tid >> 3; e < 256; e += 32) {
+            const uint32_t v = lut_bits<B>(tl, uint32_t(e & M)) | (lut_bits<B>(tl, uint32_t((e >> B) & M)) << 16);
+            *reinterpret_cast<u32x4 *>(lds_all + offset + e * 256 + 16 * (tid & 7)) = u32x4{v, v, v, v};
         }
     };
-    if constexpr (KB == 4) fill_pair_table(klut, 0, std::integral_constant<int, 4>{});
-    if constexpr (VB == 4) fill_pair_table(vlut, 128, std::integral_constant<int, 4>{});
-    if constexpr (KB == 3) fill_pair_table(klut, kKOff, std::integral_constant<int, 3>{});
-    if constexpr (VB == 3) fill_pair_table(vlut, kVOff, std::integral_constant<int, 3>{});
+    if constexpr (pair_table<KB>()) fill_byte_table(klut, 0, std::integral_constant<int, KB>{});
+    if constexpr (pair_table<VB>()) fill_byte_table(vlut, 128, std::integral_constant<int, VB>{});
 
     // ---- rotated queries, once per block: wave 0 rotates the block's 4 heads
     // (q' = D1 H D2 q / sqrt(d), [TQ+ guide] §5.3): lane l holds coordinates
@@ -373,28 +378,40 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     const float * const qsrc = qst;
     constexpr int64_t qstride = 2 * kD;
 
-    half4 aq[2][2], au[2];
+    // Key operand of the logits (16x16x32 MFMA, rows = query parts, columns =
+    // tokens): lane l holds row l % 16 at k-slots 8 (l / 16) .. + 7 of each of
+    // the 4 k-steps ks, i.e. dims 32 (l / 16) + pos(8 ks + e) of code block
+    // l / 16; rows 0..3 are the fp16 hi parts of heads 0..3, rows 4..7 the lo
+    // parts, rows 8..15 zero.
+    half8 aqk[4];
     {
-        const int h = lane & 3;
-        const float * qrow = qsrc + h * qstride;
+        const int row = lane & 15, bl = lane >> 4;
+        const float * qrow = qsrc + (row & 3) * qstride;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = qrow[32 * bl + decoded_code_of_pos<KB>(8 * ks + e)];
+                const _Float16 hi = static_cast<_Float16>(x);
+                const _Float16 lo = static_cast<_Float16>(x - static_cast<float>(hi));
+                aqk[ks][e] = row < 4 ? hi : row < 8 ? lo : static_cast<_Float16>(0.f);
+            }
+    }
+    // QJL keys: S q' as the broadcast A operand of the 4x4x4 sign products
+    // (block gs % 16 of k-step gs holds head lane & 3 at dims of k-step gs).
+    // fp16 suffices: the sketch term is a small correction weighted by the
+    // residual norm, so 2^-11 relative error in S q' stays far below the
+    // logit tolerance.
+    half4 au[2];
+    if constexpr (QJL) {
+        const float * qrow = qsrc + (lane & 3) * qstride;
 #pragma unroll
         for (int set = 0; set < 2; ++set) {
             const int gs = (lane >> 2) + 16 * set;
             const int bl = gs >> 3, kk = gs & 7;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int kpos = decoded_code_of_pos<KB>(4 * kk + i);
-                const float x = qrow[32 * bl + kpos];
-                const _Float16 hi = static_cast<_Float16>(x);
-                aq[set][0][i] = hi;
-                aq[set][1][i] = static_cast<_Float16>(x - static_cast<float>(hi));
-                if constexpr (QJL) {
-                    // fp16 suffices: the sketch term is a small correction
-                    // (weighted by the residual norm), so 2^-11 relative error
-                    // in S q' stays far below the logit tolerance
-                    au[set][i] = static_cast<_Float16>(qrow[kD + 32 * bl + sign_bit_of_pos(4 * kk + i)]);
-                }
-            }
+            for (int i = 0; i < 4; ++i)
+                au[set][i] = static_cast<_Float16>(qrow[kD + 32 * bl + sign_bit_of_pos(4 * kk + i)]);
         }
     }
     const uint32_t lane_off = uint32_t(lane & 31) * 4;  // pair-table copy of this lane
@@ -426,40 +443,49 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
                                  (lane & 3) == 2 ? 0x3C00u : (lane & 3) == 3 ? 0x3C000000u : 0u);
 
     auto process = [&](int64_t j0, const regs & r) {
-        // ---------------- logits: lane l <- 4 heads of token j0 + l.  Four
-        // independent accumulator chains (query hi / lo parts x even / odd
-        // k-steps) keep dependent MFMAs apart.
-        floatx4 Sc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        if constexpr (pair_table<KB>()) {
-            auto klook = [&](int p) {
-                if constexpr (KB == 4)
-                    return *reinterpret_cast<const uint32_t *>(tab_bytes + byte_pair_offset(r.kw, p, lane_off));
-                else
-                    return *reinterpret_cast<const uint32_t *>(tab_bytes + kKOff + pair_offset<KB>(r.kw, p, lane_off));
-            };
+        // ---------------- logits, 16 tokens per 16x16x32 MFMA chain: the B
+        // operand of lane l is 8 decoded values of code block l / 16 of token
+        // 16 tg + l % 16 (columns = tokens), so D[tg] holds the hi parts of the
+        // 4 heads in lanes 0..15 and the lo parts in lanes 16..31.  Two row
+        // swaps add the parts and place token group tg in row tg: lane l <- 4
+        // heads of token j0 + l.
+        floatx4 D[4];
 #pragma unroll
-            for (int gs = 0; gs < 32; ++gs) {
-                const uint32_t lo = klook(2 * gs);
-                const uint32_t hi = klook(2 * gs + 1);
-                const half4 bk = as_half4(lo, hi);
-                Sc[2 * (gs & 1)] = mfma4_bcast(gs & 15, aq[gs >> 4][0], bk, Sc[2 * (gs & 1)]);
-                Sc[2 * (gs & 1) + 1] = mfma4_bcast(gs & 15, aq[gs >> 4][1], bk, Sc[2 * (gs & 1) + 1]);
+        for (int tg = 0; tg < 4; ++tg) {
+            const uint32_t * wb = r.kw + KB * tg;
+            D[tg] = floatx4{0.f, 0.f, 0.f, 0.f};
+            uint32_t bq[16];
+            if constexpr (KB == 4) {
+#pragma unroll
+                for (int p = 0; p < 16; ++p)
+                    bq[p] = *reinterpret_cast<const uint32_t *>(tab_bytes + byte_pair_offset(wb, p, lane_off));
+            } else if constexpr (KB == 3) {
+                const block3_shifts sh = shift_block3(wb);
+#pragma unroll
+                for (int p = 0; p < 16; ++p)
+                    bq[p] = *reinterpret_cast<const uint32_t *>(tab_bytes + byte3_pair_offset(sh, p, lane_off));
+            } else {
+                unpack_block<KB>(klut, wb, bq);
             }
-        } else {
 #pragma unroll
-            for (int bl = 0; bl < 4; ++bl) {
-                uint32_t bq[16];
-                unpack_block<KB>(klut, r.kw + KB * bl, bq);
+            for (int ks = 0; ks < 4; ++ks)
+                D[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aqk[ks], as_half8(bq + 4 * ks), D[tg], 0, 0, 0);
+        }
+        floatx4 S;
+        {
+            floatx4 P0, P1;
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    const int gs = 8 * bl + kk;
-                    const half4 bk = as_half4(bq[2 * kk], bq[2 * kk + 1]);
-                    Sc[2 * (gs & 1)] = mfma4_bcast(gs & 15, aq[gs >> 4][0], bk, Sc[2 * (gs & 1)]);
-                    Sc[2 * (gs & 1) + 1] = mfma4_bcast(gs & 15, aq[gs >> 4][1], bk, Sc[2 * (gs & 1) + 1]);
-                }
+            for (int h = 0; h < kG; ++h) {
+                // rows: D0 = [hi0, lo0, 0, 0] and D1 = [hi1, lo1, 0, 0] -> [hi0, hi1] + [lo0, lo1]
+                const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(D[0][h]), __float_as_uint(D[1][h]), false, false);
+                const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(D[2][h]), __float_as_uint(D[3][h]), false, false);
+                P0[h] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+                P1[h] = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+                // [s0, s1, 0, 0] and [s2, s3, 0, 0] -> [s0, s1, s2, s3]
+                const auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(P0[h]), __float_as_uint(P1[h]), false, false);
+                S[h] = __uint_as_float(z[0]);
             }
         }
-        floatx4 S = (Sc[0] + Sc[2]) + (Sc[1] + Sc[3]);
         if constexpr (QJL) {
             floatx4 Sq[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -516,21 +542,28 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
 #pragma unroll
         for (int hp = 0; hp < kPasses; ++hp) {
             uint32_t o[16];
-            if constexpr (pair_table<VB>()) {
+            if constexpr (VB == 4) {
 #pragma unroll
                 for (int p = 0; p < 16; ++p)
-                    o[p] = VB == 4 ? *reinterpret_cast<const uint32_t *>(tab_bytes + byte_pair_offset(r.vw[hp], p, lane_off | 128u))
-                                   : *reinterpret_cast<const uint32_t *>(tab_bytes + kVOff + pair_offset<VB>(r.vw[hp], p, lane_off));
+                    o[p] = *reinterpret_cast<const uint32_t *>(tab_bytes + byte_pair_offset(r.vw[hp], p, lane_off | 128u));
+            } else if constexpr (VB == 3) {
+                const block3_shifts sh = shift_block3(r.vw[hp]);
+#pragma unroll
+                for (int p = 0; p < 16; ++p)
+                    o[p] = *reinterpret_cast<const uint32_t *>(tab_bytes + byte3_pair_offset(sh, p, lane_off | 128u));
             } else {
                 unpack_block<VB>(vlut, r.vw[hp], o);
             }
             const half4 aw = tr_read4(ptile, kPass * hp * 8 + p_off);
+            // all 8 transposes first, then the products: each product reads a
+            // transpose result a few instructions later, not at once
+            floatx4 t[8];
 #pragma unroll
-            for (int gd = 0; gd < 8; ++gd) {
-                const floatx4 t = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(o[2 * gd], o[2 * gd + 1]), ident,
-                                                                     floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                acc[gd] = __builtin_amdgcn_mfma_f32_4x4x4f16(aw, to_half4(t), acc[gd], 0, 0, 0);
-            }
+            for (int gd = 0; gd < 8; ++gd)
+                t[gd] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(o[2 * gd], o[2 * gd + 1]), ident,
+                                                           floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+            for (int gd = 0; gd < 8; ++gd) acc[gd] = __builtin_amdgcn_mfma_f32_4x4x4f16(aw, to_half4(t[gd]), acc[gd], 0, 0, 0);
         }
     };
 
@@ -539,9 +572,10 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     // Waves sharing a SIMD are otherwise served oldest first, which leaves the
     // youngest finishing alone; a wave drops its issue priority by one level
     // per quarter of its range done, so lagging waves catch up.
-    const int64_t span = w_end > w_begin ? w_end - w_begin : 1;
+    const int64_t span = w_end > w_begin ? w_end - w_begin : 0;
+    const int64_t q1 = w_begin + span / 4, q2 = w_begin + span / 2, q3 = w_end - span / 4;
     for (int64_t j0 = w_begin; j0 < w_end; j0 += NS * kStep) {
-        switch (static_cast<int>((j0 - w_begin) * 4 / span)) {
+        switch (int(j0 >= q1) + int(j0 >= q2) + int(j0 >= q3)) {
             case 0: __builtin_amdgcn_s_setprio(3); break;
             case 1: __builtin_amdgcn_s_setprio(2); break;
             case 2: __builtin_amdgcn_s_setprio(1); break;

@@ -194,4 +194,32 @@ __device__ __forceinline__ uint32_t byte_pair_offset(const uint32_t * w, int p, 
     return __builtin_amdgcn_perm(w[p >> 2], base_byte, 0x0C0C0000u | ((4u + uint32_t(p & 3)) << 8));
 }
 
+// 3-bit codes use the same 256-entry byte tables: the pair of codes 2p,
+// 2p + 1 of a 32-code block (3 dwords) starts at bit 6p, so in the block
+// shifted right by 6p mod 8 (0, 2, 4 or 6 bits) it starts at a byte
+// boundary; that byte (both codes plus two bits of the next code) indexes
+// the table, whose entries ignore their top two index bits.  shifted[k]
+// holds the block shifted right by 2k bits (shifted[0] = the block).
+struct block3_shifts {
+    uint32_t w[4][3];
+};
+
+__device__ __forceinline__ block3_shifts shift_block3(const uint32_t * w) {
+    block3_shifts s;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) s.w[0][i] = w[i];
+#pragma unroll
+    for (int k = 1; k < 4; ++k) {
+        s.w[k][0] = __builtin_amdgcn_alignbit(w[1], w[0], 2 * k);
+        s.w[k][1] = __builtin_amdgcn_alignbit(w[2], w[1], 2 * k);
+        s.w[k][2] = w[2] >> (2 * k);
+    }
+    return s;
+}
+
+__device__ __forceinline__ uint32_t byte3_pair_offset(const block3_shifts & s, int p, uint32_t base_byte) {
+    const int o = 6 * p, sh = o & 7, bi = (o - sh) >> 3;
+    return byte_pair_offset(s.w[sh >> 1], bi, base_byte);
+}
+
 }  // namespace tq

@@ -3,8 +3,7 @@
 Each case builds the whole workload on the GPU (every batch element and KV
 head, full context) and calls tq_encode / tq_attend_decode with the sizes,
 t_max and workspace the benchmark uses, so the launch configuration (chunk
-split, block count, static or counter-driven step assignment) is the one
-that is timed.  For a few sampled (batch, KV head) pairs the oracle encodes
+split, block count) is the one that is timed.  For a few sampled (batch, KV head) pairs the oracle encodes
 that head's K and V in float64; the GPU encoding of the head is compared
 with it, then replaced by it, so the sampled heads' decode inputs come from
 the oracle alone; their query heads' outputs are compared with the oracle's
@@ -78,7 +77,7 @@ def _run(name, pairs, lens_fn):
     del K, V
     torch.cuda.synchronize()
     out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=DEV)
-    ws = torch.empty(tq.attend_workspace_bytes(kctx, vctx, w.B, w.Hq, w.Hkv, w.T), dtype=torch.uint8,
+    ws = torch.zeros(tq.attend_workspace_bytes(kctx, vctx, w.B, w.Hq, w.Hkv, w.T), dtype=torch.uint8,
                      device=DEV)
     kc, vc = oracle_config(kctx), oracle_config(vctx)
     qn = q.cpu().numpy().astype(np.float64)

@@ -212,11 +212,14 @@ def test_attend_reuses_one_workspace():
     ctx = tq.Context(seed=9, head_dim=d, bits=3)
     kg, vg = tq.PackedPlanes.from_numpy(kp), tq.PackedPlanes.from_numpy(vp)
     ws = torch.zeros(tq.attend_workspace_bytes(ctx, ctx, B, Hkv * G, Hkv, T), dtype=torch.uint8, device=DEV)
-    for lens in ([T, 17], [1, 2999], [0, 64], [T, T]):
+    # the workspace holds completion counters that every call leaves at zero,
+    # also across calls whose t_max (and so chunk split) differs
+    for lens, t_max in (([T, 17], T), ([1, 2999], T), ([0, 64], T), ([T, T], T), ([40, 700], 700),
+                        ([300, 2], 300), ([T, 1000], T)):
         lens = np.array(lens, dtype=np.int32)
         ref = odec.attend_decode(q.astype(np.float64), kp, vp, kc, vc, lens)
         out = tq.attend_decode(ctx, ctx, torch.from_numpy(q).to(DEV), kg, vg, torch.from_numpy(lens).to(DEV),
-                               t_max=T, workspace=ws)
+                               t_max=t_max, workspace=ws)
         torch.cuda.synchronize()
         _say("workspace reuse", lens.tolist(), assert_attend_close(out.cpu().numpy().astype(np.float64), ref))
 
