@@ -230,17 +230,28 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(const dev_tables kt
     }
 }
 
+// Sign word i of a rotation sign vector held in the kernel arguments, picked
+// by selects among the (scalar) words: indexing the argument array with a
+// per-lane index would be a memory load on the critical path.
+template <int D>
+__device__ __forceinline__ uint32_t sign_word(const uint32_t * w, int i) {
+    uint32_t r = w[0];
+#pragma unroll
+    for (int k = 1; k < (D + 31) / 32; ++k) r = i == k ? w[k] : r;
+    return r;
+}
+
 // Log-sum-exp merge of the per-chunk states of one (batch, query head), then
 // the inverse rotation o = R^T o' back to the original domain.  One pass:
-// wave w owns chunks [32 w, 32 w + 32), [32 w + 128, ...), ...; each batch's
-// loads (m, l and the lane's dims lane + 64 i of every chunk) are all issued
-// before any is used, and the wave keeps a running maximum.  The four waves'
-// states are combined through LDS, and wave 0 applies R^T with the
-// Walsh-Hadamard butterflies run across lanes (no block barriers).
+// the chunks are dealt to the four waves round-robin, CB per wave per batch;
+// each batch's loads (m, l and the lane's dims lane + 64 i of every chunk)
+// are all issued before any is used, and the wave keeps a running maximum.
+// The four waves' states are combined through LDS, and wave 0 applies R^T
+// with the Walsh-Hadamard butterflies run across lanes (no block barriers).
 template <int D>
 __global__ __launch_bounds__(256) void attend_merge_kernel(const dev_tables vt, const attend_args a) {
     constexpr int PER = D >= 64 ? D / 64 : 1;  // dims per lane
-    constexpr int CB = 32;                     // chunks per wave per batch
+    constexpr int CB = 16;                     // chunks per wave per batch
     __shared__ float wm[4], wl[4];
     __shared__ float wacc[4][PER * 64];
     const int h = blockIdx.x, b = blockIdx.y;
@@ -251,12 +262,12 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(const dev_tables vt, 
     float M = -INFINITY, l = 0.f, acc[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-    for (int c0 = wave * CB; c0 < n; c0 += 4 * CB) {
+    for (int c0 = 0; c0 < n; c0 += 4 * CB) {
         float mc[CB], lc[CB], vc[CB][PER];
 #pragma unroll
         for (int u = 0; u < CB; ++u) {
-            const int c = c0 + u;
-            const float * p = base + int64_t(c < n ? c : c0) * (D + 2);
+            const int c = c0 + 4 * u + wave;
+            const float * p = base + int64_t(c < n ? c : 0) * (D + 2);
             mc[u] = c < n ? p[0] : -INFINITY;
             lc[u] = p[1];
 #pragma unroll
@@ -306,7 +317,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(const dev_tables vt, 
         for (int w = 0; w < 4; ++w) o = fmaf(sw[w], wacc[w][dim], o);
         o *= inv;
         // o_orig = R^T o = D2 . H . D1 . o / sqrt(d)
-        if (dim < D && ((vt.d1[dim >> 5] >> (dim & 31)) & 1)) o = -o;
+        if (dim < D && ((sign_word<D>(vt.d1, dim >> 5) >> (dim & 31)) & 1)) o = -o;
         x[i] = dim < D ? o : 0.f;
     }
     // butterflies: strides of 64 and up inside the lane, below 64 across lanes
@@ -333,7 +344,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(const dev_tables vt, 
         const int dim = lane + 64 * i;
         if (dim < D) {
             float y = x[i] * rs;
-            if ((vt.d2[dim >> 5] >> (dim & 31)) & 1) y = -y;
+            if ((sign_word<D>(vt.d2, dim >> 5) >> (dim & 31)) & 1) y = -y;
             a.out[(int64_t(b) * a.Hq + h) * D + dim] = y;
         }
     }
