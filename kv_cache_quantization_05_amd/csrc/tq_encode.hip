@@ -493,6 +493,17 @@ __device__ __forceinline__ uint32_t dbl_add(uint32_t c, bool bit) {
     return __builtin_addc(c, c, bit ? 1u : 0u, &co);
 }
 
+// 2c + bit with the bits of all lanes given as a wave mask (a compare result,
+// possibly combined with others by scalar logic): one v_addc whose carry-in
+// is the mask, where the compiler would turn each bit into a select and a
+// shift-or.  (A plain ALU instruction: no memory access in the asm.)
+__device__ __forceinline__ uint32_t shift_in(uint32_t c, uint64_t bits) {
+    uint32_t r;
+    uint64_t carry_out;
+    asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(c), "s"(bits));
+    return r;
+}
+
 template <int D, int BITS, bool PREFETCH>
 __global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, const encode_args a,
                                                           const grid_index gi, const uint32_t nvec) {
@@ -666,13 +677,15 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, co
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hA[tt][__builtin_popcount(b & bi) & 1], xb[bi], acc, 0, 0, 0);
                 u[tt] = acc;
             }
+            // each decision is a wave mask; the bits are shifted in from
+            // the masks (sign flips by scalar XORs)
             uint32_t c = 0;
 #pragma unroll
             for (int j = 7; j >= 0; --j) {
                 const float y = u[j >> 2][j & 3];
                 const float ya = fabsf(y);
-                const bool neg = y < 0.f;
-                c = dbl_add(c, !neg);
+                const uint64_t neg = __ballot(y < 0.f);
+                c = shift_in(c, ~neg);
                 if constexpr (BITS == 4) {
                     const bool t1 = ya > T[3];
                     const float q2 = t1 ? T[5] : T[1];
@@ -680,17 +693,17 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, co
                     const float lo3 = t1 ? T[4] : T[0];
                     const bool t2 = ya > q2;
                     const bool t3 = ya > (t2 ? hi3 : lo3);
-                    c = dbl_add(c, t1 != neg);
-                    c = dbl_add(c, t2 != neg);
-                    c = dbl_add(c, t3 != neg);
+                    c = shift_in(c, __ballot(t1) ^ neg);
+                    c = shift_in(c, __ballot(t2) ^ neg);
+                    c = shift_in(c, __ballot(t3) ^ neg);
                 } else if constexpr (BITS == 3) {
                     const bool t1 = ya > T[1];
                     const bool t2 = ya > (t1 ? T[2] : T[0]);
-                    c = dbl_add(c, t1 != neg);
-                    c = dbl_add(c, t2 != neg);
+                    c = shift_in(c, __ballot(t1) ^ neg);
+                    c = shift_in(c, __ballot(t2) ^ neg);
                 } else {
                     const bool t1 = ya > T[0];
-                    c = dbl_add(c, t1 != neg);
+                    c = shift_in(c, __ballot(t1) ^ neg);
                 }
             }
             c = nrm > 0.0 ? c ^ xm[b] : zero_chunk;
