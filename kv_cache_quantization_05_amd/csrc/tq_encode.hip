@@ -299,6 +299,13 @@ __device__ __forceinline__ f16x8 as_f16x8(uint4 w) {
     return r;
 }
 
+// v with its sign flipped when bit e of w is set, as a bit XOR on the high word
+__device__ __forceinline__ double flip_sign(double v, uint32_t w, int e) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+    const uint64_t m = static_cast<uint64_t>((w << (31 - e)) & 0x80000000u) << 32;
+    return __longlong_as_double(static_cast<long long>(b ^ m));
+}
+
 // QJL ctx.  Phase A (per lane, one 32-coordinate block of one vector): the
 // rotation, z, codes, residual r = z - c[code] and gamma = ||r|| / sqrt(d) in
 // double (so gamma's fp16 rounding matches float64); r goes to LDS as an
@@ -317,8 +324,8 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(const dev_tables t, con
     constexpr int RT = D / 16;       // 16-row tiles of S (m = d)
     constexpr int KS = D / 32;       // 32-wide k-steps
     constexpr int CT = VPB / 16;     // 16-vector column tiles
-    constexpr int CB = CT < 4 ? CT : 4;
     __shared__ __align__(16) uint16_t rl[2][VPB * RS];
+    __shared__ int64_t pvs[VPB];  // plane index of each vector of the batch (-1: none)
     __shared__ float cpos[8];  // positive centroids cb[2^(b-1) + k]
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -353,9 +360,11 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(const dev_tables t, con
         nsq = group_sum<LPV>(nsq);
         const double n = sqrt(nsq);
         if (valid && blk == 0) a.out.norms[pv] = half_bits_rne(n);
+        if (blk == 0) pvs[vl] = valid ? pv : int64_t(-1);
+        // D2 as sign-bit XORs (a per-element select would be hoisted into 32
+        // scalar lane masks, more than the scalar registers hold)
 #pragma unroll
-        for (int e = 0; e < 32; ++e)
-            if ((d2w >> e) & 1) x[e] = -x[e];
+        for (int e = 0; e < 32; ++e) x[e] = flip_sign(x[e], d2w, e);
         lane_fwht(x);
         cross_lane_fwht<LPV>(x, blk);
         // z = sqrt(d) R x / n = D1 y / n;  code = #{k : th_k < z}, decided on
@@ -371,8 +380,7 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(const dev_tables t, con
         uint32_t rh[16], rlo[16];
 #pragma unroll
         for (int e = 0; e < 32; ++e) {
-            double z = x[e] * inv_n;
-            if ((d1w >> e) & 1) z = -z;
+            const double z = flip_sign(x[e] * inv_n, d1w, e);
             const float zf = static_cast<float>(z);
             const uint32_t kk = count_below<BITS>(fabsf(zf), pth);
             const bool zneg = !(zf > 0.f);  // z = 0 (zero vectors) counts no threshold: 2^(b-1) - 1
@@ -413,44 +421,53 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(const dev_tables t, con
         }
         __syncthreads();
 
-        // ---------------- phase B: rows 16 rt .. +15 of h for 16 vectors per tile
+        // ---------------- phase B: rows 16 rt .. +15 of h for 16 vectors per
+        // tile; wave w takes row tiles w, w + 4, ..., and every residual tile
+        // read from LDS feeds all of them
         const int n16 = lane & 15, g4 = lane >> 4;
-        for (int rt = wave; rt < RT; rt += 4) {
+        constexpr int RW = (RT + 3) / 4;  // row tiles per wave (waves >= RT have none at d = 32)
+        f32x4 acc[RW][CT];
 #pragma unroll
-            for (int c0 = 0; c0 < CT; c0 += CB) {
-                f32x4 acc[CB];
+        for (int rw = 0; rw < RW; ++rw)
 #pragma unroll
-                for (int c = 0; c < CB; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int c = 0; c < CT; ++c) acc[rw][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // one k-step at a time (a full unroll hoists every load and spills)
+#pragma unroll 1
+        for (int ks = 0; ks < KS; ++ks) {
+            f16x8 ah[RW], al[RW];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const int64_t so = int64_t(16 * rt + n16) * D + 32 * ks + 8 * g4;
-                    const f16x8 ah = as_f16x8(*reinterpret_cast<const uint4 *>(s_hi + so));
-                    const f16x8 al = as_f16x8(*reinterpret_cast<const uint4 *>(s_lo + so));
+            for (int rw = 0; rw < RW; ++rw) {
+                const int rt = wave + 4 * rw < RT ? wave + 4 * rw : 0;
+                const int64_t so = int64_t(16 * rt + n16) * D + 32 * ks + 8 * g4;
+                ah[rw] = as_f16x8(*reinterpret_cast<const uint4 *>(s_hi + so));
+                al[rw] = as_f16x8(*reinterpret_cast<const uint4 *>(s_lo + so));
+            }
 #pragma unroll
-                    for (int c = 0; c < CB; ++c) {
-                        const int ro = (16 * (c0 + c) + n16) * RS + 32 * ks + 8 * g4;
-                        const f16x8 bh = as_f16x8(*reinterpret_cast<const uint4 *>(&rl[0][ro]));
-                        const f16x8 bl = as_f16x8(*reinterpret_cast<const uint4 *>(&rl[1][ro]));
-                        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc[c], 0, 0, 0);
-                        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl, acc[c], 0, 0, 0);
-                        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc[c], 0, 0, 0);
-                    }
+            for (int c = 0; c < CT; ++c) {
+                const int ro = (16 * c + n16) * RS + 32 * ks + 8 * g4;
+                const f16x8 bh = as_f16x8(*reinterpret_cast<const uint4 *>(&rl[0][ro]));
+                const f16x8 bl = as_f16x8(*reinterpret_cast<const uint4 *>(&rl[1][ro]));
+#pragma unroll
+                for (int rw = 0; rw < RW; ++rw) {
+                    acc[rw][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rw], bh, acc[rw][c], 0, 0, 0);
+                    acc[rw][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rw], bl, acc[rw][c], 0, 0, 0);
+                    acc[rw][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[rw], bh, acc[rw][c], 0, 0, 0);
                 }
-                // lane holds rows 16 rt + 4 g4 + i of vector 16 (c0 + c) + n16
+            }
+        }
+        // lane holds rows 16 rt + 4 g4 + i of vector 16 c + n16
 #pragma unroll
-                for (int c = 0; c < CB; ++c) {
-                    uint32_t bits = 0;
+        for (int c = 0; c < CT; ++c) {
+            const int64_t pvv = pvs[16 * c + n16];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) bits |= (acc[c][i] > 0.f ? 1u : 0u) << (4 * g4 + i);
-                    bits |= __shfl_xor(bits, 16);
-                    bits |= __shfl_xor(bits, 32);
-                    const uint32_t vv = base + 16 * (c0 + c) + n16;
-                    if (g4 == 0 && vv < nvec) {
-                        int64_t xo, pvv;
-                        vector_offsets(vv, a, gi, xo, pvv);
-                        reinterpret_cast<uint16_t *>(a.out.signs + pvv * (D / 8))[rt] = static_cast<uint16_t>(bits);
-                    }
-                }
+            for (int rw = 0; rw < RW; ++rw) {
+                uint32_t bits = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) bits |= (acc[rw][c][i] > 0.f ? 1u : 0u) << (4 * g4 + i);
+                bits |= __shfl_xor(bits, 16);
+                bits |= __shfl_xor(bits, 32);
+                if (g4 == 0 && pvv >= 0 && wave + 4 * rw < RT)
+                    reinterpret_cast<uint16_t *>(a.out.signs + pvv * (D / 8))[wave + 4 * rw] = static_cast<uint16_t>(bits);
             }
         }
         __syncthreads();  // the residual tile is rewritten by the next iteration
