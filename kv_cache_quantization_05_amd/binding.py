@@ -182,8 +182,17 @@ class PackedPlanes:
         return tuple(self.norms.shape)
 
     def c_struct(self):
-        """Planes struct; strides in vectors from the norms tensor (3-D grid, padded in front)."""
+        """Planes struct; strides in vectors from the norms tensor (3-D grid, padded in front).
+        Every plane must share the norms' vector layout (its per-vector
+        bytes contiguous), since the C ABI carries one set of strides."""
         st = list(self.norms.stride())
+        for name, t in (("codes", self.codes), ("signs", self.signs), ("rnorms", self.rnorms)):
+            if t is None:
+                continue
+            per = t.shape[-1] if name in ("codes", "signs") else 1
+            lead = list(t.stride())[:-1] if name in ("codes", "signs") else list(t.stride())
+            if (name in ("codes", "signs") and t.stride(-1) != 1) or lead != [x * per for x in st]:
+                raise ValueError(f"{name} plane layout does not match the norms plane's vector strides")
         st = [0] * (3 - len(st)) + st
         p = Planes()
         p.codes = self.codes.data_ptr()

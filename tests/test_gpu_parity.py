@@ -224,6 +224,36 @@ def test_attend_reuses_one_workspace():
         _say("workspace reuse", lens.tolist(), assert_attend_close(out.cpu().numpy().astype(np.float64), ref))
 
 
+@pytest.mark.parametrize("kb,vb,qjl", [(3, 3, False), (4, 4, True), (2, 4, False)])
+def test_attend_token_strided_planes(kb, vb, qjl):
+    """Caches laid out [B, T, Hkv] (heads interleaved per token), passed as
+    [B, Hkv, T] views: the token stride is Hkv vectors, not one."""
+    d, B, Hkv, G, T = 128, 2, 2, 4, 1500
+    kc = oenc.Config(seed=6, head_dim=d, bits=kb, qjl=qjl)
+    vc = oenc.Config(seed=6, head_dim=d, bits=vb)
+    rng = np.random.default_rng(60 + kb)
+    k = rng.standard_normal((B, T, Hkv, d)) * 1.5
+    v = rng.standard_normal((B, T, Hkv, d))
+    q = rng.standard_normal((B, Hkv * G, d)).astype(np.float32)
+    kp, vp = _oracle_planes(k, kc), _oracle_planes(v, vc)   # planes over [B, T, Hkv]
+    lens = np.array([T, 901], dtype=np.int32)
+    to_bht = lambda pl: {n: np.ascontiguousarray(np.swapaxes(a, 1, 2)) for n, a in pl.items()}  # noqa: E731
+    ref = odec.attend_decode(q.astype(np.float64), to_bht(kp), to_bht(vp), kc, vc, lens)
+
+    def view(pl):
+        g = tq.PackedPlanes.from_numpy(pl)
+        sw = lambda t: t.transpose(1, 2) if t is not None else None  # noqa: E731
+        return tq.PackedPlanes(sw(g.codes), sw(g.norms), sw(g.signs), sw(g.rnorms))
+
+    kg, vg = view(kp), view(vp)
+    assert kg.norms.stride(2) == Hkv
+    kctx = tq.Context(seed=6, head_dim=d, bits=kb, qjl=qjl)
+    vctx = tq.Context(seed=6, head_dim=d, bits=vb)
+    out = tq.attend_decode(kctx, vctx, torch.from_numpy(q).to(DEV), kg, vg, torch.from_numpy(lens).to(DEV))
+    torch.cuda.synchronize()
+    _say("token-strided planes", kb, vb, qjl, assert_attend_close(out.cpu().numpy().astype(np.float64), ref))
+
+
 @pytest.mark.parametrize("kb,vb,qjl", [(3, 3, False), (4, 4, True)])
 def test_attend_long_context_counts_every_token_once(kb, vb, qjl):
     """At long contexts each (batch, KV head) is split over many blocks and
