@@ -59,9 +59,17 @@ struct grid_index {
 };
 
 // Offsets of vector v of the [n0, n1, n2] grid: input element offset and
-// output plane index.  v < 2^32 (checked on the host).
+// output plane index.  v < 2^32 (checked on the host).  FLAT: the host has
+// folded the grid into its last dimension (n0 = n1 = 1) with both strides
+// in [0, 2^32), so each offset is one 32 x 32 -> 64-bit product.
+template <bool FLAT = false>
 __device__ __forceinline__ void vector_offsets(uint32_t v, const encode_args & a, const grid_index & gi,
                                                int64_t & xoff, int64_t & pv) {
+    if constexpr (FLAT) {
+        xoff = static_cast<int64_t>(uint64_t(v) * static_cast<uint32_t>(a.xs2));
+        pv = static_cast<int64_t>(uint64_t(v) * static_cast<uint32_t>(a.out.stride[2]));
+        return;
+    }
     const uint32_t r = fdiv(v, gi.n2);
     const uint32_t i2 = v - r * gi.n2.d;
     const uint32_t i0 = fdiv(r, gi.n1);
@@ -504,6 +512,14 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint32_t (&w)[4]) {
     return r;
 }
 
+// The value unchanged, but opaque to the optimiser: what is computed from it
+// inside a rarely taken branch stays there instead of being hoisted into the
+// common path.  (An empty asm: no instruction is emitted.)
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 // 2c + bit, as one add-with-carry whose carry-in is the (per-lane) bit
 __device__ __forceinline__ uint32_t dbl_add(uint32_t c, bool bit) {
     unsigned int co;
@@ -521,7 +537,7 @@ __device__ __forceinline__ uint32_t shift_in(uint32_t c, uint64_t bits) {
     return r;
 }
 
-template <int D, int BITS, bool PREFETCH>
+template <int D, int BITS, bool PREFETCH, bool FLAT>
 __global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, const encode_args a,
                                                           const grid_index gi, const uint32_t nvec) {
     constexpr int NB = D / 32;
@@ -579,15 +595,17 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, co
 
     // each wave takes 16 vectors per iteration; with PREFETCH the next
     // iteration's inputs are loaded while the current ones are processed
+    // (unconditionally: lanes past the end load the last vector again, so
+    // the loaded registers need no loop-carried copies)
     const uint32_t stride = gridDim.x * 64;
     uint32_t wn[NB][4];
     int64_t pv_next = 0;
     bool valid_next = false;
-    auto load_inputs = [&](uint32_t bs) {
-        const uint32_t v = bs + n;
+    auto load_inputs = [&](uint64_t bs) {
+        const uint64_t v = bs + n;
         valid_next = v < nvec;
         int64_t xoff;
-        vector_offsets(valid_next ? v : nvec - 1, a, gi, xoff, pv_next);
+        vector_offsets<FLAT>(valid_next ? static_cast<uint32_t>(v) : nvec - 1, a, gi, xoff, pv_next);
         const uint16_t * src = static_cast<const uint16_t *>(a.x) + xoff + 8 * g;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -598,7 +616,7 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, co
             wn[b][3] = q.w;
         }
     };
-    uint32_t base = blockIdx.x * 64 + wave * 16;
+    uint64_t base = blockIdx.x * 64 + wave * 16;
     if (PREFETCH && base < nvec) load_inputs(base);
     for (; base < nvec; base += stride) {
         if (!PREFETCH) load_inputs(base);
@@ -610,12 +628,12 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, co
         for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int j = 0; j < 4; ++j) w[b][j] = wn[b][j] ^ m2[b][j];
-        if (PREFETCH && base + stride < nvec) load_inputs(base + stride);
+        if (PREFETCH) load_inputs(base + stride);
 
         // Norm, as float64 rounds it to fp16.  First in fp32 from exact bf16
         // products (v_dot2): its error stays below 19 fp32 ulps of n (32
-        // roundings of positive partial sums, the lane sum and the square
-        // root), so unless n lies within 32 ulps of an fp16 rounding midpoint
+        // roundings of positive partial sums, the lane sum, and v_sqrt_f32's
+        // 1-ulp result), so unless n lies within 32 ulps of an fp16 rounding midpoint
         // it rounds to the same fp16 as float64.  Those vectors, and norms
         // outside fp16's normal range [2^-14, 60000] (where the midpoint test
         // does not apply; products may also be subnormal), take the float64
@@ -628,7 +646,7 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, co
             for (int j = 0; j < 4; ++j) s32 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[b][j]), as_bf16x2(w[b][j]), s32, false);
         s32 += __shfl_xor(s32, 16);
         s32 += __shfl_xor(s32, 32);
-        const float n32 = sqrtf(s32);
+        const float n32 = __builtin_amdgcn_sqrtf(s32);
         const int mid = int(__float_as_uint(n32) & 0x1FFFu) - 0x1000;
         const bool exact64 = (mid > -32 && mid < 32) || !(n32 >= 0x1p-14f && n32 <= 60000.f);
         double nrm = n32;
@@ -639,7 +657,8 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, co
             for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const double lo = bf16_lo(w[b][j]), hi = bf16_hi(w[b][j]);
+                    const uint32_t wj = opaque(w[b][j]);
+                    const double lo = bf16_lo(wj), hi = bf16_hi(wj);
                     nsq = fma(lo, lo, nsq);
                     nsq = fma(hi, hi, nsq);
                 }
@@ -662,8 +681,9 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, co
             for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const uint32_t lo = __float_as_uint(bf16_lo(w[b][j]) * sc) >> 16;
-                    const uint32_t hi = __float_as_uint(bf16_hi(w[b][j]) * sc) & 0xFFFF0000u;
+                    const uint32_t wj = opaque(w[b][j]);
+                    const uint32_t lo = __float_as_uint(bf16_lo(wj) * sc) >> 16;
+                    const uint32_t hi = __float_as_uint(bf16_hi(wj) * sc) & 0xFFFF0000u;
                     w[b][j] = lo | hi;
                 }
             if (far) nf = static_cast<float>(ldexp(nrm, -e));
@@ -739,6 +759,39 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, co
     }
 }
 
+// The grid folded into one dimension when its vectors are evenly spaced in
+// both the input and the planes (size-1 dimensions dropped, each remaining
+// dimension's strides equal to the folded inner block's extent), with both
+// strides in [0, 2^32).  Returns false, leaving f unset, otherwise.
+bool fold_flat(const encode_args & a, encode_args & f) {
+    const int64_t n[3] = {a.n0, a.n1, a.n2}, xs[3] = {a.xs0, a.xs1, a.xs2};
+    const int64_t ps[3] = {a.out.stride[0], a.out.stride[1], a.out.stride[2]};
+    int64_t cn = 1, cx = 0, cp = 0;
+    bool any = false;
+    for (int i = 2; i >= 0; --i) {
+        if (n[i] == 1) continue;
+        if (!any) {
+            cn = n[i];
+            cx = xs[i];
+            cp = ps[i];
+            any = true;
+        } else {
+            if (xs[i] != cn * cx || ps[i] != cn * cp) return false;
+            cn *= n[i];
+        }
+    }
+    constexpr int64_t kLim = int64_t(1) << 32;
+    if (cx < 0 || cx >= kLim || cp < 0 || cp >= kLim) return false;
+    f = a;
+    f.n0 = f.n1 = 1;
+    f.n2 = cn;
+    f.xs0 = f.xs1 = 0;
+    f.xs2 = cx;
+    f.out.stride[0] = f.out.stride[1] = 0;
+    f.out.stride[2] = cp;
+    return true;
+}
+
 template <int D, int BITS, bool QJL>
 hipError_t launch_encode_dtype(const dev_tables & t, const encode_args & a, uint32_t nvec, hipStream_t s) {
     constexpr int VPB = 256 / (D / 32);
@@ -761,7 +814,7 @@ hipError_t launch_encode_dtype(const dev_tables & t, const encode_args & a, uint
             static std::atomic<int> per_cu_cache{0};  // same on every gfx950 device
             int per_cu = per_cu_cache.load(std::memory_order_relaxed);
             if (per_cu == 0) {
-                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, encode_mfma_kernel<DM, BITS, true>, 256, 0) !=
+                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, encode_mfma_kernel<DM, BITS, true, false>, 256, 0) !=
                         hipSuccess ||
                     per_cu <= 0)
                     per_cu = 4;
@@ -770,12 +823,20 @@ hipError_t launch_encode_dtype(const dev_tables & t, const encode_args & a, uint
             const int cap = current_cu_count() * per_cu;
             const int64_t need = (int64_t(nvec) + 63) / 64;
             const int64_t iters = (need + cap - 1) / cap;
+            encode_args f;
+            const bool flat = fold_flat(a, f);
             if (iters <= 4) {
                 const int64_t mb = (need + iters - 1) / iters;
-                hipLaunchKernelGGL((encode_mfma_kernel<DM, BITS, true>), dim3(mb), dim3(256), 0, s, t, a, gi, nvec);
+                if (flat)
+                    hipLaunchKernelGGL((encode_mfma_kernel<DM, BITS, true, true>), dim3(mb), dim3(256), 0, s, t, f, gi, nvec);
+                else
+                    hipLaunchKernelGGL((encode_mfma_kernel<DM, BITS, true, false>), dim3(mb), dim3(256), 0, s, t, a, gi, nvec);
             } else {
                 const int64_t mb = need < 256 * 16 ? need : 256 * 16;
-                hipLaunchKernelGGL((encode_mfma_kernel<DM, BITS, false>), dim3(mb), dim3(256), 0, s, t, a, gi, nvec);
+                if (flat)
+                    hipLaunchKernelGGL((encode_mfma_kernel<DM, BITS, false, true>), dim3(mb), dim3(256), 0, s, t, f, gi, nvec);
+                else
+                    hipLaunchKernelGGL((encode_mfma_kernel<DM, BITS, false, false>), dim3(mb), dim3(256), 0, s, t, a, gi, nvec);
             }
         } else if (bf16)
             hipLaunchKernelGGL((encode_kernel<D, BITS, true>), dim3(blocks), dim3(256), 0, s, t, a, gi, nvec);

@@ -93,6 +93,83 @@ def test_encode_strided_grid_into_cache_layout():
     assert np.all(got["codes"][:, :, T:] == 0) and np.all(got["norms"][:, :, T:] == 0)
 
 
+@pytest.mark.parametrize("d,bits,strided", [(64, 4, False), (128, 3, False), (128, 3, True)])
+def test_encode_many_vectors(d, bits, strided):
+    # more vectors than a few rounds of resident blocks cover, so the encoder
+    # takes its grid-striding loop; contiguous and strided ([B, T, H, d]
+    # read as a [B, H, T] grid) inputs
+    _say("encode many", d, bits, strided)
+    ctx = tq.Context(seed=5, head_dim=d, bits=bits)
+    B, H = 2, 8
+    T = 600_000 // (B * H) if d == 64 else 400_000 // (B * H)
+    if strided:
+        xs = _x((B, T, H, d), torch.bfloat16, seed=d + 1, scale_ch=False)
+        x = xs.permute(0, 2, 1, 3)
+    else:
+        x = _x((B, H, T, d), torch.bfloat16, seed=d + 2, scale_ch=False)
+        xs = x
+    xg = xs.to(DEV)
+    planes = tq.encode(ctx, xg.permute(0, 2, 1, 3) if strided else xg)
+    torch.cuda.synchronize()
+    cfg = oracle_config(ctx)
+    ref = oenc.encode(x.float().numpy().astype(np.float64), cfg)
+    _say(compare_encode(planes.numpy(), ref, cfg))
+
+
+def _integer_rows(d, n, seed):
+    """Integer-valued vectors whose rotated coordinates are often exactly 0:
+    all ones, pairs of unit vectors, and sparse or small random integers."""
+    rng = np.random.default_rng(seed)
+    rows = [np.ones(d), np.eye(d)[0] + np.eye(d)[1], np.eye(d)[0] - np.eye(d)[3]]
+    while len(rows) < n:
+        k = len(rows) % 3
+        if k == 0:
+            rows.append(rng.choice([-1.0, 0.0, 1.0], size=d, p=[0.25, 0.5, 0.25]))
+        elif k == 1:
+            rows.append(rng.integers(-3, 4, size=d).astype(np.float64))
+        else:
+            v = np.zeros(d)
+            v[rng.choice(d, size=2, replace=False)] = rng.choice([-1.0, 1.0], size=2)
+            rows.append(v)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
+@pytest.mark.parametrize("bits,qjl", [(2, False), (3, False), (4, False), (3, True)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_encode_exact_ties_at_zero(d, bits, qjl, dtype):
+    # An integer vector's rotated coordinate D1 H D2 x is an exact integer,
+    # often 0.  z = 0 lies exactly on the middle threshold: the centroids
+    # -c and +c either side of it are equally near, so codes 2^(b-1) - 1
+    # and 2^(b-1) are both nearest-centroid codes there (the oracle's
+    # float64 product lands a rounding error either side of 0).  Everywhere
+    # else the codes must match as usual; norms are exact.
+    _say("encode ties", d, bits, qjl, dtype)
+    ctx = tq.Context(seed=13, head_dim=d, bits=bits, qjl=qjl)
+    cfg = oracle_config(ctx)
+    xi = _integer_rows(d, 96, seed=d + bits)
+    xi = np.concatenate([xi, 0.375 * xi[:32]])              # exact in bf16 too
+    x = torch.from_numpy(xi).to(dtype)
+    planes = tq.encode(ctx, x.to(DEV)).numpy()
+    torch.cuda.synchronize()
+    ref = oenc.encode(x.float().numpy().astype(np.float64), cfg)
+    signs = np.sign(oenc.get_tables(cfg).R)                # D1 H D2 entries, +-1
+    y_exact = xi @ signs.T                                   # exact integers
+    tie = y_exact == 0
+    assert tie.sum() > xi.shape[0], "inputs must produce many exact zeros"
+    g_code = oenc.unpack_bits_lsb(planes["codes"], bits, d)
+    half = 1 << (bits - 1)
+    assert np.all((g_code[tie] == half - 1) | (g_code[tie] == half))
+    differs = ((g_code != ref["code"]) & tie).any(axis=-1)  # vectors whose tie choices differ
+    assert np.array_equal(planes["norms"], ref["norms"])
+    keep = ~differs
+    sub = {k: v[keep] for k, v in planes.items() if v is not None}
+    rsub = {k: (v[keep] if isinstance(v, np.ndarray) and v.shape[:1] == (xi.shape[0],) else v)
+            for k, v in ref.items()}
+    _say("tie entries", int(tie.sum()), "vectors with another tie choice", int(differs.sum()),
+         compare_encode(sub, rsub, cfg) if keep.any() else "none left")
+
+
 def test_encode_empty_grid_is_noop():
     ctx = tq.Context(seed=0, head_dim=128, bits=3)
     x = torch.zeros((0, 128), device=DEV)
