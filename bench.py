@@ -163,7 +163,8 @@ def bench_search(args, w):
         # the scorer is an fp16 matrix-core contraction (algorithmic flops:
         # 2d + 2m per query-key pair) against the dense fp16 MFMA peak
         "roofline": {"kernel": "scores", "bound": "mfma", "achieved": round(tflops, 3), "peak": 2500.0,
-                     "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4),
+                     "traffic": traffic_from_profiles("scores", w.name),
                      "flops_per_launch": flops, "avg_ms": round(sc_ms, 5)},
         "roofline_encode": {"kernel": "encode", "bound": "hbm",
                             "achieved": round(enc_bytes / (enc_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,

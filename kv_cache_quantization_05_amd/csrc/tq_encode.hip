@@ -489,9 +489,10 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(const dev_tables t, con
 // of the coordinate), so H_d D2 x is a 32-point transform of every block,
 // u_b = H_32 (D2 x)_b, followed by an (d/32)-point transform across blocks.
 // The 32-point part is a 16x16x32 bf16 MFMA per block and 16-row half, with
-// the inputs as the B operand exactly as loaded (bf16, D2 applied as sign
-// XORs) and H_32's +-1 entries as the A operand: products are exact and the
-// sums accumulate in fp32, as in the VALU butterflies.  A wave takes 16
+// the inputs as the B operand exactly as loaded (bf16) and the +-1 entries
+// of H_32 D2_b as the A operand (D2 and the cross-block signs folded into
+// the tiles): products are exact and the sums accumulate in fp32, as in the
+// VALU butterflies.  A wave takes 16
 // vectors; lane l loads coordinates 8(l/16)..+7 of each block of vector
 // l%16.  The A rows are permuted so that the same lane receives output
 // coordinates 8(l/16)..+7 of each block: the cross-block transform, the
@@ -538,7 +539,7 @@ __device__ __forceinline__ uint32_t shift_in(uint32_t c, uint64_t bits) {
 }
 
 template <int D, int BITS, bool PREFETCH, bool FLAT>
-__global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, const encode_args a,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void encode_mfma_kernel(const dev_tables t, const encode_args a,
                                                           const grid_index gi, const uint32_t nvec) {
     constexpr int NB = D / 32;
     constexpr uint32_t kHalf = 1u << (BITS - 1);
@@ -568,8 +569,7 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, co
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) hwn[tt][j] = hw[tt][j] ^ 0x80008000u;
-    const bf16x8 hA[2][2] = {{as_bf16x8(hw[0]), as_bf16x8(hwn[0])}, {as_bf16x8(hw[1]), as_bf16x8(hwn[1])}};
-    // D2 as sign XORs of the loaded bf16 pairs
+    // D2's signs for the lane's input columns (bit 15: even, bit 31: odd)
     uint32_t m2[NB][4];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -577,6 +577,22 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, co
         for (int j = 0; j < 4; ++j) {
             const int e = 8 * g + 2 * j;
             m2[b][j] = (((t.d2[b] >> e) & 1) << 15) | (((t.d2[b] >> (e + 1)) & 1) << 31);
+        }
+    // D2 folded into the A operand's columns: tile (tt, bi, s) is
+    // (-1)^s H_32 D2_bi, so the B operand is the input exactly as loaded
+    bf16x8 hA[2][NB][2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int bi = 0; bi < NB; ++bi) {
+            uint32_t p[4], m[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                p[j] = hw[tt][j] ^ m2[bi][j];
+                m[j] = hwn[tt][j] ^ m2[bi][j];
+            }
+            hA[tt][bi][0] = as_bf16x8(p);
+            hA[tt][bi][1] = as_bf16x8(m);
         }
     // D1 (all bits of a code whose z changes sign) as XORs of the lane's
     // 8-code chunks; and the chunk of a zero vector
@@ -622,12 +638,12 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, co
         if (!PREFETCH) load_inputs(base);
         const bool valid = valid_next;
         const int64_t pv = pv_next;
-        // inputs with D2 applied (sign XORs); the norm does not see the signs
+        // the inputs as loaded (D2 sits in the A operand)
         uint32_t w[NB][4];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) w[b][j] = wn[b][j] ^ m2[b][j];
+            for (int j = 0; j < 4; ++j) w[b][j] = wn[b][j];
         if (PREFETCH) load_inputs(base + stride);
 
         // Norm, as float64 rounds it to fp16.  First in fp32 from exact bf16
@@ -694,11 +710,11 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, co
         bf16x8 xb[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) xb[b] = as_bf16x8(w[b]);
-        // Codes of coordinates 32 b + 8 g + j, j = 4 tt + r, as 8-code chunks,
-        // built bit-serially from the top: chunk = 2 chunk + bit, each bit a
-        // compare result (code(z) = count of positive thresholds below |z|,
-        // with every bit flipped when z < 0, and 2^(b-1) set for z >= 0).
-        // One output block at a time keeps 8 accumulators live.
+        // Codes of coordinates 32 b + 8 g + j, j = 4 tt + r, as 8-code chunks
+        // (code(z) = count of positive thresholds below |z|, with every bit
+        // flipped when z < 0, and 2^(b-1) set for z >= 0; a coordinate of
+        // exactly 0 is a tie between the two middle codes).  One output block
+        // at a time keeps 8 accumulators live.
         float T[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) T[j] = p[j] * nf;
@@ -711,18 +727,18 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, co
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int bi = 0; bi < NB; ++bi)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hA[tt][__builtin_popcount(b & bi) & 1], xb[bi], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hA[tt][bi][__builtin_popcount(b & bi) & 1], xb[bi], acc, 0, 0, 0);
                 u[tt] = acc;
             }
-            // each decision is a wave mask; the bits are shifted in from
-            // the masks (sign flips by scalar XORs)
+            // each 8-code chunk is built bit-serially from the top: the sign
+            // bit straight from y, then each magnitude decision as a wave
+            // mask shifted in by one add-with-carry
             uint32_t c = 0;
 #pragma unroll
             for (int j = 7; j >= 0; --j) {
                 const float y = u[j >> 2][j & 3];
                 const float ya = fabsf(y);
-                const uint64_t neg = __ballot(y < 0.f);
-                c = shift_in(c, ~neg);
+                c = __builtin_amdgcn_alignbit(c, __float_as_uint(y), 31);  // the sign bit
                 if constexpr (BITS == 4) {
                     const bool t1 = ya > T[3];
                     const float q2 = t1 ? T[5] : T[1];
@@ -730,20 +746,27 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(const dev_tables t, co
                     const float lo3 = t1 ? T[4] : T[0];
                     const bool t2 = ya > q2;
                     const bool t3 = ya > (t2 ? hi3 : lo3);
-                    c = shift_in(c, __ballot(t1) ^ neg);
-                    c = shift_in(c, __ballot(t2) ^ neg);
-                    c = shift_in(c, __ballot(t3) ^ neg);
+                    c = shift_in(c, __ballot(t1));
+                    c = shift_in(c, __ballot(t2));
+                    c = shift_in(c, __ballot(t3));
                 } else if constexpr (BITS == 3) {
                     const bool t1 = ya > T[1];
                     const bool t2 = ya > (t1 ? T[2] : T[0]);
-                    c = shift_in(c, __ballot(t1) ^ neg);
-                    c = shift_in(c, __ballot(t2) ^ neg);
+                    c = shift_in(c, __ballot(t1));
+                    c = shift_in(c, __ballot(t2));
                 } else {
                     const bool t1 = ya > T[0];
-                    c = shift_in(c, __ballot(t1) ^ neg);
+                    c = shift_in(c, __ballot(t1));
                 }
             }
-            c = nrm > 0.0 ? c ^ xm[b] : zero_chunk;
+            {
+                // fields are [sign, magnitude bits]: flip the magnitude bits of
+                // negative coordinates and every sign bit
+                constexpr uint32_t low = BITS == 2 ? 0x5555u : BITS == 3 ? 0x249249u : 0x11111111u;
+                const uint32_t m = (c >> (BITS - 1)) & low;
+                const uint32_t spread = m * ((1u << (BITS - 1)) - 1);
+                c = nrm > 0.0 ? c ^ spread ^ (xm[b] ^ (low << (BITS - 1))) : zero_chunk;
+            }
             if constexpr (BITS == 4) {
                 if (valid) reinterpret_cast<uint32_t *>(row + 16 * b)[g] = c;
             } else if constexpr (BITS == 3) {
