@@ -789,22 +789,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
 bool fold_flat(const encode_args & a, encode_args & f) {
     const int64_t n[3] = {a.n0, a.n1, a.n2}, xs[3] = {a.xs0, a.xs1, a.xs2};
     const int64_t ps[3] = {a.out.stride[0], a.out.stride[1], a.out.stride[2]};
-    int64_t cn = 1, cx = 0, cp = 0;
+    constexpr int64_t kLim = int64_t(1) << 32;
+    int64_t cn = 1, cx = 0, cp = 0;  // cn < 2^32: the host has checked n0 n1 n2 < 2^32
     bool any = false;
     for (int i = 2; i >= 0; --i) {
         if (n[i] == 1) continue;
         if (!any) {
+            if (xs[i] < 0 || xs[i] >= kLim || ps[i] < 0 || ps[i] >= kLim) return false;
             cn = n[i];
             cx = xs[i];
             cp = ps[i];
             any = true;
         } else {
-            if (xs[i] != cn * cx || ps[i] != cn * cp) return false;
+            // cn, cx, cp < 2^32: the products fit in 64 unsigned bits
+            if (xs[i] < 0 || ps[i] < 0 || uint64_t(xs[i]) != uint64_t(cn) * uint64_t(cx) ||
+                uint64_t(ps[i]) != uint64_t(cn) * uint64_t(cp))
+                return false;
             cn *= n[i];
         }
     }
-    constexpr int64_t kLim = int64_t(1) << 32;
-    if (cx < 0 || cx >= kLim || cp < 0 || cp >= kLim) return false;
     f = a;
     f.n0 = f.n1 = 1;
     f.n2 = cn;
