@@ -7,13 +7,18 @@
 // bit packing, and the optional 1-bit QJL sketch of the residual
 // ([Orión plan] Fase 3 sign-bit sketch; [TQ explainer] §2.2).
 //
-// Work mapping: a vector of d coordinates is owned by d/32 consecutive lanes;
-// lane `blk` holds coordinates 32*blk .. 32*blk+31, which is exactly one
-// packed 32-code block, so each lane writes its own block.  The first five
-// butterfly stages run inside a lane's registers, the remaining log2(d/32)
-// stages exchange with partner lanes (DPP quad permutes / ds_swizzle).
+// Three kernels:
+//  * encode_mfma_kernel (bf16 inputs, d = 64 or 128, MSE-only): the rotation
+//    as exact-product bf16 matrix-core tiles and a wave-mask quantiser; its
+//    own comment below gives the lane layout.
+//  * encode_kernel (other MSE-only inputs) and encode_qjl_kernel: a vector of
+//    d coordinates is owned by d/32 consecutive lanes; lane `blk` holds
+//    coordinates 32*blk .. 32*blk+31, which is exactly one packed 32-code
+//    block, so each lane writes its own block.  The first five butterfly
+//    stages run inside a lane's registers, the remaining log2(d/32) stages
+//    exchange with partner lanes (DPP quad permutes / ds_swizzle).
 //
-// Two precisions:
+// Precision of the lane-per-block kernels:
 //  * MSE-only ctx (encode_kernel): the norm is accumulated in double (fp16
 //    norms must round exactly as a float64 evaluation does), the rotation in
 //    fp32.  A code can then differ from a float64 evaluation only within
@@ -538,6 +543,8 @@ __device__ __forceinline__ uint32_t shift_in(uint32_t c, uint64_t bits) {
     return r;
 }
 
+// At most 128 VGPRs (4 waves per SIMD; no spills): at 130 the prefetching
+// kernel would drop to 3 waves and to the slower non-prefetching launch plan.
 template <int D, int BITS, bool PREFETCH, bool FLAT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void encode_mfma_kernel(const dev_tables t, const encode_args a,
                                                           const grid_index gi, const uint32_t nvec) {
