@@ -51,6 +51,20 @@ def traffic_from_profiles(kernel, workload):
     return ent.get("bytes_per_launch")
 
 
+def _cpu_threads():
+    """(threads the oracle's numpy uses, the BLAS pool size): numpy's
+    matrix products run on the BLAS pool, everything else on one thread."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] + [1])
+    except Exception:
+        blas = 1
+    return blas, blas
+
+
+DTYPE = "f16 mfma, f32 acc"   # decode: fp16 matrix-core products, fp32 accumulation
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The float64 oracle on the host cores, on a bounded slice of the same
     workload: one batch element, one KV head (its Hq/Hkv query heads) and the
@@ -62,11 +76,7 @@ def cpu_baseline(w, budget_s=12.0):
     from oracle import decode as odec
     from oracle import encode as oenc
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count()
+    cores, blas = _cpu_threads()
     G = w.Hq // w.Hkv
     kc = oenc.Config(seed=w.seed, head_dim=w.d, bits=w.k_bits, qjl=w.k_qjl)
     vc = oenc.Config(seed=w.seed, head_dim=w.d, bits=w.v_bits)
@@ -98,6 +108,7 @@ def cpu_baseline(w, budget_s=12.0):
     return {"value": round(dec_gbs, 6), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
             "sample": f"batch 0, KV head 0 ({G} query heads), first {Ts} positions; "
                       f"encode {enc_s:.2f} s, decode {dec_s:.2f} s; float64 numpy",
+            "host_cpus": os.cpu_count(), "blas_threads": int(blas),
             "encode_mtok_s": round(enc_mtoks, 6)}
 
 
@@ -154,7 +165,7 @@ def bench_search(args, w):
         "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE, "data": "synthetic",
         "config": {"workload": w.name, "n": n, "n_queries": nq, "head_dim": w.d, "bits": w.k_bits,
                    "qjl": w.k_qjl, "top_k": k_top, "packed_bytes": int(packed)},
         "scores_ms": round(sc_ms, 4),
@@ -172,7 +183,61 @@ def bench_search(args, w):
                             "traffic": traffic_from_profiles("encode", w.name), "algorithmic_bytes": int(enc_bytes),
                             "avg_ms": round(enc_ms, 5)},
     }
+    line["recall_at_10"] = search_recall(X, Q, idx, k_top)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_search(w, bpv)
     print(json.dumps(line), flush=True)
+
+
+def search_recall(X, Q, idx, k, n_sample=32):
+    """Recall@k of the GPU's top-k (from the packed codes) against the exact
+    float64 inner-product top-k of the unquantised vectors, on a fixed
+    sample of queries (a quality figure beside the throughput)."""
+    import torch
+
+    sel = torch.arange(0, Q.shape[0], Q.shape[0] // n_sample)[:n_sample]
+    exact = Q[sel.to(Q.device)].double().cpu() @ X.double().cpu().T
+    top = torch.topk(exact, k, dim=1).indices
+    got = idx[sel.to(idx.device)].cpu()
+    hits = [len(set(got[r].tolist()) & set(top[r].tolist())) for r in range(len(sel))]
+    return round(sum(hits) / (k * len(sel)), 4)
+
+
+def cpu_baseline_search(w, bpv, budget_s=12.0):
+    """The float64 oracle on the host cores for the search workload: encode
+    of N_s database vectors, then every query's scores against them (plain
+    dequantise-then-dot) and its top-k, N_s doubled up to about a quarter of
+    the budget.  value = packed bytes of the N_s keys per second of scoring
+    all queries, the unit of the GPU line."""
+    import numpy as np
+
+    from kv_cache_quantization_05_amd import workloads as wl
+    from oracle import decode as odec
+    from oracle import encode as oenc
+
+    cores, blas = _cpu_threads()
+    cfg = oenc.Config(seed=w.seed, head_dim=w.d, bits=w.k_bits, qjl=w.k_qjl)
+    oenc.get_tables(cfg)
+    Ns = 1024
+    X, Q = wl.search_set(w, "cpu", n=65536)
+    Qn = Q.double().numpy()
+    while True:
+        x = X[:Ns].double().numpy()
+        t0 = time.perf_counter()
+        p = oenc.encode(x, cfg)
+        t1 = time.perf_counter()
+        pl = {k: p[k] for k in ("codes", "norms", "signs", "rnorms") if k in p}
+        odec.top_k(odec.scores(Qn, pl, cfg), w.extra["top_k"])
+        t2 = time.perf_counter()
+        if t2 - t0 > budget_s / 4 or Ns * 2 > X.shape[0]:
+            break
+        Ns *= 2
+    enc_s, sc_s = t1 - t0, t2 - t1
+    return {"value": round(Ns * bpv / sc_s / 1e9, 6), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {Ns} database vectors, all {Q.shape[0]} queries: encode {enc_s:.2f} s, "
+                      f"scores + top-{w.extra['top_k']} {sc_s:.2f} s; float64 numpy",
+            "host_cpus": os.cpu_count(), "blas_threads": int(blas),
+            "encode_mtok_s": round(Ns / enc_s / 1e6, 6)}
 
 
 def main():
@@ -180,7 +245,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama_t32k")
+    ap.add_argument("--workload", default="llama_b4_t128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--min-rotation-bytes", type=float, default=1.1 * 2**30)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -281,7 +346,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": DTYPE,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "Hkv": w.Hkv, "Hq": w.Hq, "head_dim": w.d,
                    "k_bits": w.k_bits, "v_bits": w.v_bits, "k_qjl": w.k_qjl, "input": w.in_dtype,
@@ -291,7 +356,7 @@ def main():
         "decode_us_p10_p90": [round(dec_ms[len(dec_ms) // 10] * 1e3, 2), round(dec_ms[(9 * len(dec_ms)) // 10] * 1e3, 2)],
         "encode_us": round(enc_avg * 1e3, 2),
         "encode_mtok_s": round(enc_mtoks, 2),
-        "roofline": r_enc if enc_avg > dec_avg else r_dec,
+        "roofline": r_dec,
         "roofline_decode": r_dec,
         "roofline_encode": r_enc,
     }

@@ -254,23 +254,76 @@ def attend_workspace_bytes(k_ctx, v_ctx, B, Hq, Hkv, t_max):
     return lib().tq_attend_decode_workspace(k_ctx.handle, v_ctx.handle, B, Hq, Hkv, t_max)
 
 
+def _check_query(q, ctx, ndim, what="q"):
+    """The C ABI carries no shapes or dtypes for q: check them here."""
+    if not isinstance(q, torch.Tensor) or q.dim() != ndim:
+        raise ValueError(f"{what} must be a {ndim}-D tensor")
+    if q.dtype != torch.float32:
+        raise ValueError(f"{what} must be float32")
+    if not q.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if q.shape[-1] != ctx.head_dim:
+        raise ValueError(f"{what} has last dim {q.shape[-1]}, the context's head_dim is {ctx.head_dim}")
+
+
+def _check_planes(p, ctx, grid_prefix, what):
+    if p.codes.shape[-1] != ctx.code_bytes or tuple(p.codes.shape[:-1]) != tuple(p.grid):
+        raise ValueError(f"{what} planes do not match the context's code bytes per vector")
+    if ctx.qjl and (p.signs is None or p.rnorms is None or p.signs.shape[-1] != ctx.sign_bytes):
+        raise ValueError(f"{what} planes lack the QJL sign/rnorm planes of the context")
+    if tuple(p.grid[:len(grid_prefix)]) != tuple(grid_prefix):
+        raise ValueError(f"{what} planes have grid {p.grid}, expected leading dims {grid_prefix}")
+
+
+def _check_on_gpu(*tensors):
+    """Every tensor handed to libtq must live on one GPU (checked last, so the
+    shape and dtype checks above also run on a host without a GPU)."""
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1 or next(iter(devs)).type != "cuda":
+        raise ValueError("q, planes, seq_lens and outputs must all be on the same GPU")
+
+
+def _plane_tensors(p):
+    return (p.codes, p.norms, p.signs, p.rnorms)
+
+
+def _workspace(ws, need, device):
+    """A caller's workspace is passed as (pointer, bytes): it must be a
+    contiguous uint8 tensor on the GPU of the other arguments."""
+    if ws is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    if ws.dtype != torch.uint8 or not ws.is_contiguous() or ws.device != device:
+        raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
+    return ws
+
+
 def attend_decode(k_ctx: Context, v_ctx: Context, q: torch.Tensor, k: PackedPlanes, v: PackedPlanes,
                   seq_lens: torch.Tensor, t_max=None, scale=None, out=None, workspace=None, stream=None):
     """tq_attend_decode.  q: fp32 [B, Hq, d]; k, v: planes over [B, Hkv, Tcap];
     seq_lens: int32 [B] on the GPU; returns fp32 [B, Hq, d]."""
+    _check_query(q, k_ctx, 3)
     B, Hq, d = q.shape
+    if len(k.grid) != 3 or len(v.grid) != 3:
+        raise ValueError("k and v planes must cover a 3-D grid [B, Hkv, Tcap]")
     Hkv = k.grid[1]
+    _check_planes(k, k_ctx, (B, Hkv), "k")
+    _check_planes(v, v_ctx, (B, Hkv), "v")
+    if not isinstance(seq_lens, torch.Tensor) or seq_lens.dtype != torch.int32 or seq_lens.numel() != B \
+            or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 tensor of B entries")
     if t_max is None:
         t_max = k.grid[2]
     if t_max > k.grid[2] or t_max > v.grid[2]:
         raise ValueError("t_max exceeds the cache capacity of the planes")
     if scale is None:
         scale = d ** -0.5
+    if out is not None and (out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != (B, Hq, d)):
+        raise ValueError("out must be a contiguous float32 [B, Hq, d] tensor")
+    _check_on_gpu(q, seq_lens, out, *_plane_tensors(k), *_plane_tensors(v))
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     need = attend_workspace_bytes(k_ctx, v_ctx, B, Hq, Hkv, t_max)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
     _check(lib().tq_attend_decode(k_ctx.handle, v_ctx.handle, _ptr(q), k.c_struct(), v.c_struct(),
                                   _ptr(seq_lens), B, Hq, Hkv, t_max, ctypes.c_float(scale), _ptr(out),
                                   _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
@@ -287,19 +340,25 @@ def scores(k_ctx: Context, q: torch.Tensor, k: PackedPlanes, top_k=0, scale=1.0,
 
     top_k == 0 returns the full [n_q, n_k] score matrix; otherwise
     (scores [n_q, top_k], indices [n_q, top_k]) best first."""
+    _check_query(q, k_ctx, 2)
     n_q = q.shape[0]
+    if len(k.grid) != 1:
+        raise ValueError("k planes must cover a 1-D grid [n_k]")
+    _check_planes(k, k_ctx, (), "k")
     n_k = k.grid[-1]
-    if top_k == 0:
-        if out is None:
-            out = torch.empty((n_q, n_k), dtype=torch.float32, device=q.device)
-    else:
-        if out is None:
-            out = torch.empty((n_q, top_k), dtype=torch.float32, device=q.device)
-        if out_idx is None:
-            out_idx = torch.empty((n_q, top_k), dtype=torch.int64, device=q.device)
+    shape = (n_q, n_k) if top_k == 0 else (n_q, top_k)
+    if out is not None and (out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != shape):
+        raise ValueError(f"out must be a contiguous float32 {shape} tensor")
+    if top_k > 0 and out_idx is not None and (out_idx.dtype != torch.int64 or not out_idx.is_contiguous()
+                                              or tuple(out_idx.shape) != shape):
+        raise ValueError(f"out_idx must be a contiguous int64 {shape} tensor")
+    _check_on_gpu(q, out, out_idx if top_k > 0 else None, *_plane_tensors(k))
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=q.device)
+    if top_k > 0 and out_idx is None:
+        out_idx = torch.empty(shape, dtype=torch.int64, device=q.device)
     need = scores_workspace_bytes(k_ctx, n_q, n_k, top_k)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
     _check(lib().tq_scores(k_ctx.handle, _ptr(q), n_q, ctypes.c_float(scale), k.c_struct(), n_k, top_k,
                            _ptr(out), _ptr(out_idx), _ptr(workspace), workspace.numel(),
                            _stream_ptr(stream)))

@@ -67,6 +67,29 @@ def scores(q, k_planes, cfg: Config, scale=1.0):
     return scale * (np.asarray(q, dtype=np.float64) @ k_hat.T)
 
 
+def scores_rotated(q, k_planes, cfg: Config, scale=1.0):
+    """The same logits in the form the pages' fused path reaches them, for
+    large key sets: the query is rotated once and scored against the stored
+    centroids (<q, R^T c> = <R q, c>, [TQ+ guide] §5.3 pre-rotate-queries),
+    and a QJL key adds its sketch term against S R q, so no key is ever
+    rebuilt in the original domain:
+        s = scale * N * ( <R q, c[code]> / sqrt(d)
+                          + gamma * sqrt(pi/2) / m * <S R q, sigma> ).
+    Equal to scores() up to float64 rounding (pinned by a test)."""
+    t = get_tables(cfg)
+    d = cfg.head_dim
+    q = np.asarray(q, dtype=np.float64)
+    rq = q @ t.R.T                                     # R q, one per query
+    code = codes_of(k_planes, cfg)
+    n16 = fp16_value(k_planes["norms"])
+    s = (t.c[code] @ rq.T) / math.sqrt(d)              # [n_k, n_q]
+    if cfg.qjl:
+        sigma = 2.0 * unpack_bits_lsb(k_planes["signs"], 1, cfg.m) - 1.0
+        g16 = fp16_value(k_planes["rnorms"])
+        s = s + (g16 * math.sqrt(math.pi / 2.0) / cfg.m)[:, None] * (sigma @ (rq @ t.S.T).T)
+    return scale * (s * n16[:, None]).T
+
+
 def attend_decode(q, k_planes, v_planes, k_cfg: Config, v_cfg: Config, seq_lens, scale=None):
     """Decode attention for q[B, Hq, d] against planes laid out [B, Hkv, T, ...].
 

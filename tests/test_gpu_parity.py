@@ -160,14 +160,12 @@ def test_encode_exact_ties_at_zero(d, bits, qjl, dtype):
     g_code = oenc.unpack_bits_lsb(planes["codes"], bits, d)
     half = 1 << (bits - 1)
     assert np.all((g_code[tie] == half - 1) | (g_code[tie] == half))
-    differs = ((g_code != ref["code"]) & tie).any(axis=-1)  # vectors whose tie choices differ
     assert np.array_equal(planes["norms"], ref["norms"])
-    keep = ~differs
-    sub = {k: v[keep] for k, v in planes.items() if v is not None}
-    rsub = {k: (v[keep] if isinstance(v, np.ndarray) and v.shape[:1] == (xi.shape[0],) else v)
-            for k, v in ref.items()}
-    _say("tie entries", int(tie.sum()), "vectors with another tie choice", int(differs.sum()),
-         compare_encode(sub, rsub, cfg) if keep.any() else "none left")
+    # every entry off the exact ties is compared, in every vector; for QJL
+    # contexts gamma and the signs are compared on the vectors whose tie
+    # choices agree (the residual depends on the chosen centroid)
+    rep = compare_encode(planes, ref, cfg, tie_ok=tie)
+    _say("tie entries", int(tie.sum()), "tie choices that differ", int(((g_code != ref["code"]) & tie).sum()), rep)
 
 
 def test_encode_empty_grid_is_noop():
@@ -184,8 +182,8 @@ def _oracle_planes(x, cfg):
 
 
 @pytest.mark.parametrize("kb,vb,qjl,G", [(3, 3, False, 4), (4, 4, True, 4), (2, 4, False, 1),
-                                         (4, 3, False, 8), (3, 2, True, 2)])
-@pytest.mark.parametrize("d", [64, 128, 256])
+                                         (4, 4, False, 1), (4, 3, False, 8), (3, 2, True, 2)])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 def test_attend_matches_oracle(kb, vb, qjl, G, d):
     _say("attend", kb, vb, qjl, G, d)
     B, Hkv, T = 3, 2, 2600
@@ -289,8 +287,8 @@ def test_attend_reuses_one_workspace():
     ctx = tq.Context(seed=9, head_dim=d, bits=3)
     kg, vg = tq.PackedPlanes.from_numpy(kp), tq.PackedPlanes.from_numpy(vp)
     ws = torch.zeros(tq.attend_workspace_bytes(ctx, ctx, B, Hkv * G, Hkv, T), dtype=torch.uint8, device=DEV)
-    # the workspace holds completion counters that every call leaves at zero,
-    # also across calls whose t_max (and so chunk split) differs
+    # successive calls whose t_max (and so chunk split) differs share the
+    # workspace: nothing a call leaves in it may leak into the next
     for lens, t_max in (([T, 17], T), ([1, 2999], T), ([0, 64], T), ([T, T], T), ([40, 700], 700),
                         ([300, 2], 300), ([T, 1000], T)):
         lens = np.array(lens, dtype=np.int32)
@@ -405,5 +403,38 @@ def test_scores_topk_matches_oracle(k):
     s, i = tq.scores(ctx, qs.to(DEV), tq.PackedPlanes.from_numpy(kp), top_k=k)
     torch.cuda.synchronize()
     agree = assert_topk_valid(s.cpu().numpy(), i.cpu().numpy(), ref, k)
-    _say("top-k agreement", agree)
-    assert agree > 0.9
+    _say("top-k agreement with the oracle's exact list", agree)
+
+
+def test_same_inputs_give_bit_identical_outputs():
+    """Run-to-run determinism: encode, decode attention and the fused top-k,
+    each called twice on the same inputs, give bit-identical outputs (no
+    atomics or scheduling order may leak into a result)."""
+    gen = torch.Generator().manual_seed(21)
+    B, Hkv, G, T, d = 2, 8, 4, 9000, 128
+    K = torch.randn((B, Hkv, T, d), generator=gen).to(torch.bfloat16).to(DEV)
+    V = torch.randn((B, Hkv, T, d), generator=gen).to(torch.bfloat16).to(DEV)
+    q = torch.randn((B, Hkv * G, d), generator=gen).to(DEV)
+    lens = torch.tensor([T, 5001], dtype=torch.int32, device=DEV)
+    for kb, vb, qjl in ((3, 3, False), (4, 4, True)):
+        kctx = tq.Context(seed=1, head_dim=d, bits=kb, qjl=qjl)
+        vctx = tq.Context(seed=1, head_dim=d, bits=vb)
+        runs = []
+        for _ in range(2):
+            kp, vp = tq.encode(kctx, K), tq.encode(vctx, V)
+            o = tq.attend_decode(kctx, vctx, q, kp, vp, lens)
+            torch.cuda.synchronize()
+            runs.append((kp.numpy(), vp.numpy(), o.cpu().numpy()))
+        for name in runs[0][0]:
+            assert np.array_equal(runs[0][0][name], runs[1][0][name]), ("k", name)
+        for name in runs[0][1]:
+            assert np.array_equal(runs[0][1][name], runs[1][1][name]), ("v", name)
+        assert np.array_equal(runs[0][2].view(np.uint32), runs[1][2].view(np.uint32)), "decode output"
+    w = wl.WORKLOADS["search_1m"]
+    db, qs = wl.search_set(w, DEV, n=60000, n_queries=70)
+    ctx = tq.Context(seed=0, head_dim=256, bits=4, qjl=True)
+    planes = tq.encode(ctx, db)
+    r1 = [t.cpu().numpy() for t in tq.scores(ctx, qs, planes, top_k=10)]
+    r2 = [t.cpu().numpy() for t in tq.scores(ctx, qs, planes, top_k=10)]
+    assert np.array_equal(r1[0].view(np.uint32), r2[0].view(np.uint32)) and np.array_equal(r1[1], r2[1])
+    _say("bit-identical across runs: encode, decode, top-k")

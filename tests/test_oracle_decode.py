@@ -33,6 +33,21 @@ def test_pre_rotation_identity():
     assert np.max(np.abs(explicit - fused)) < 1e-12
 
 
+@pytest.mark.parametrize("bits,qjl,d", [(3, False, 128), (4, True, 256), (2, True, 32)])
+def test_rotated_scores_equal_plain_definition(bits, qjl, d):
+    # the rotated-domain form (used on large key sets) against explicit
+    # dequantisation of every key followed by a plain dot product
+    cfg = Config(seed=5, head_dim=d, bits=bits, qjl=qjl)
+    rng = np.random.default_rng(d + bits)
+    x = rng.standard_normal((300, d)) * np.exp(0.5 * rng.standard_normal(d))
+    q = rng.standard_normal((7, d))
+    planes = encode.encode(x, cfg)
+    plain = decode.scores(q, planes, cfg, scale=0.3)
+    fused = decode.scores_rotated(q, planes, cfg, scale=0.3)
+    assert fused.shape == plain.shape == (7, 300)
+    assert np.max(np.abs(fused - plain)) <= 1e-12 * np.max(np.abs(plain))
+
+
 def test_dequant_brute_force_tiny():
     # d=32 by explicit loops: x_hat_i = N/sqrt(d) * sum_k R_ki c[code_k]
     cfg = Config(seed=1, head_dim=32, bits=2)
