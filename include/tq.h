@@ -190,6 +190,23 @@ int32_t tq_attend_decode(const struct tq_ctx * k_ctx, const struct tq_ctx * v_ct
 int64_t tq_attend_decode_workspace(const struct tq_ctx * k_ctx, const struct tq_ctx * v_ctx, int32_t B,
                                    int32_t Hq, int32_t Hkv, int64_t t_max);
 
+/*
+ * tq_attend_decode without a caller workspace, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, semantics and results
+ * as tq_attend_decode; the workspace is a fixed device buffer of
+ * TQ_ATTEND_STATIC_SCRATCH_BYTES = 16 MiB held by the library on each GPU it
+ * runs on until the process ends.  Sizes whose tq_attend_decode_workspace()
+ * exceeds it give TQ_STATUS_UNSUPPORTED.  The call allocates nothing.  Every
+ * call on one GPU shares that GPU's buffer: calls that overlap on one GPU
+ * (on different streams or host threads without ordering) race and give
+ * undefined outputs.  The current device must be the contexts' device.
+ */
+int32_t tq_attend_decode_static(const struct tq_ctx * k_ctx, const struct tq_ctx * v_ctx,
+                                const float * q, struct tq_planes k, struct tq_planes v,
+                                const int32_t * seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                                int64_t t_max, float scale, float * out, void * hip_stream);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 const char * tq_last_error(void);
 

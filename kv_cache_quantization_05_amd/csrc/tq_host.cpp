@@ -34,6 +34,22 @@ int32_t ok() {
     return TQ_STATUS_OK;
 }
 
+}  // namespace
+
+int32_t tq::set_error(int32_t status, const char * fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int tq::ctx_device(const tq_ctx * ctx) { return ctx->device; }
+
+namespace {
+
 int32_t device_status(hipError_t e, const char * what) {
     if (e == hipSuccess) return ok();
     return fail(TQ_STATUS_DEVICE, "%s: %s", what, hipGetErrorString(e));

@@ -7,9 +7,18 @@
 
 #include "../../include/tq.h"
 
+// Size of the device array behind tq_attend_decode_static (16 MiB: the
+// benchmark layers need about 1.2 MB).
+#define TQ_ATTEND_STATIC_SCRATCH_BYTES (int64_t(16) << 20)
+
 namespace tq {
 
 constexpr int kMaxDim = 256;
+
+// Records the thread-local error text and returns `status` (tq_host.cpp).
+int32_t set_error(int32_t status, const char * fmt, ...) __attribute__((format(printf, 2, 3)));
+// Device a ctx is bound to.
+int ctx_device(const tq_ctx * ctx);
 
 // Small per-config tables passed to kernels by value (kernel arguments).
 // Sign masks: bit i of word i/32 set means the diagonal entry is -1.
