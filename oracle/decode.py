@@ -52,6 +52,11 @@ def dequant(planes, cfg: Config, with_qjl=None):
     use_qjl = cfg.qjl if with_qjl is None else with_qjl
     code = codes_of(planes, cfg)
     n16 = fp16_value(planes["norms"])
+    if cfg.norm_group:                                # one norm per 32-block:
+        L = cfg.group_len                             # y_b = (N_b / sqrt(32)) c[code_b]
+        cg = t.c[code].reshape(code.shape[:-1] + (d // L, L))
+        y = (n16[..., None] * cg / math.sqrt(L)).reshape(code.shape)
+        return y @ t.R                                # R^T y, row-vector form
     u = t.c[code] / math.sqrt(d)                      # rotated-domain unit estimate
     if use_qjl:
         bits = unpack_bits_lsb(planes["signs"], 1, cfg.m)
@@ -82,6 +87,11 @@ def scores_rotated(q, k_planes, cfg: Config, scale=1.0):
     rq = q @ t.R.T                                     # R q, one per query
     code = codes_of(k_planes, cfg)
     n16 = fp16_value(k_planes["norms"])
+    if cfg.norm_group:                                 # per-block norms weight each block
+        L = cfg.group_len
+        cg = t.c[code].reshape(code.shape[:-1] + (d // L, L))
+        y = (n16[..., None] * cg / math.sqrt(L)).reshape(code.shape)
+        return scale * (y @ rq.T).T
     s = (t.c[code] @ rq.T) / math.sqrt(d)              # [n_k, n_q]
     if cfg.qjl:
         sigma = 2.0 * unpack_bits_lsb(k_planes["signs"], 1, cfg.m) - 1.0

@@ -20,6 +20,16 @@ Readings (the pages are silent):
     directly from float64 (RNE);
   * z = sqrt(d) * (R x) / n (unit-norm vector scaled so coordinates are about
     N(0,1)); n == 0 gives z = 0;
+  * norm per 32-block (the layout behind the pages' 3.5-bit turbo3 figure,
+    [TQ+ guide] §1.2, against one norm per 128 values, §5.2): n_b is the
+    norm of block b of the rotated vector y = R x, z_b = sqrt(32) y_b / n_b,
+    and the norms plane holds d/32 fp16 values per vector;
+  * norm correction ([TQ+ guide] §11 names it; no formula is given): the
+    stored norm is n sqrt(L) / ||c[code]|| over the L coordinates sharing it,
+    so that the dequantised group (N / sqrt(L)) c[code] has exactly the
+    original norm n (up to the fp16 rounding of N);
+  * rotation "haar": the dense seeded QR rotation of tables.haar_rotation in
+    place of D1.H.D2 ([TQ+ guide] §3, §4);
   * code_i = #{k : tau_k < z_i} (a tie goes to the lower code);
   * codes are an LSB-first bit stream: code j of a vector occupies bits
     b*j .. b*j+b-1, bit k of the stream is bit (k % 8) of byte k // 8, so a
@@ -46,6 +56,9 @@ class Config:
     block: int = 32
     qjl: bool = False
     qjl_dim: int = 0  # 0 -> head_dim
+    rotation: str = "wht"       # "wht": D1.H.D2; "haar": dense seeded QR rotation
+    norm_group: int = 0         # 0: one norm per vector; 32: one per 32-code block
+    norm_correction: bool = False
 
     @property
     def m(self):
@@ -59,6 +72,15 @@ class Config:
     def sign_bytes(self):
         return self.m // 8 if self.qjl else 0
 
+    @property
+    def norms_per_vector(self):
+        return self.head_dim // self.norm_group if self.norm_group else 1
+
+    @property
+    def group_len(self):
+        """Coordinates sharing one stored norm."""
+        return self.norm_group or self.head_dim
+
     def check(self):
         d = self.head_dim
         if d < 32 or d > 256 or d & (d - 1):
@@ -69,6 +91,12 @@ class Config:
             raise ValueError("block must be 32")
         if self.qjl and (self.m % 8 or self.m <= 0):
             raise ValueError("qjl_dim must be a positive multiple of 8")
+        if self.rotation not in ("wht", "haar"):
+            raise ValueError("rotation must be 'wht' or 'haar'")
+        if self.norm_group not in (0, 32):
+            raise ValueError("norm_group must be 0 (per vector) or 32 (per block)")
+        if self.qjl and (self.norm_group or self.norm_correction):
+            raise ValueError("QJL keys take one plain norm per vector")
 
 
 class Tables:
@@ -78,7 +106,10 @@ class Tables:
         cfg.check()
         self.cfg = cfg
         self.d1, self.d2 = tables.rotation_signs(cfg.seed, cfg.head_dim)
-        self.R = tables.rotation_matrix(cfg.seed, cfg.head_dim)
+        if cfg.rotation == "haar":
+            self.R = tables.haar_rotation(cfg.seed, cfg.head_dim)
+        else:
+            self.R = tables.rotation_matrix(cfg.seed, cfg.head_dim)
         self.c = tables.codebook(cfg.bits)
         self.tau = tables.thresholds(cfg.bits)
         self.S = tables.gaussian_matrix(cfg.seed, cfg.m, cfg.head_dim) if cfg.qjl else None
@@ -132,14 +163,26 @@ def encode(x, cfg: Config):
     x = np.asarray(x, dtype=np.float64)
     if x.shape[-1] != d:
         raise ValueError("last axis must be head_dim")
-    n = np.sqrt(np.sum(x * x, axis=-1))                 # step 1: norm
     y = x @ t.R.T                                       # step 2: y = R x
+    L = cfg.group_len
+    if cfg.norm_group:                                  # step 1, per block: norms of the
+        yg = y.reshape(y.shape[:-1] + (d // L, L))      # rotated vector's 32-blocks
+        n = np.sqrt(np.sum(yg * yg, axis=-1))
+    else:                                               # step 1: norm of the input
+        yg = y[..., None, :]
+        n = np.sqrt(np.sum(x * x, axis=-1))[..., None]
     safe = np.where(n > 0, n, 1.0)
-    z = np.where(n[..., None] > 0, math.sqrt(d) * y / safe[..., None], 0.0)
+    z = np.where(n[..., None] > 0, math.sqrt(L) * yg / safe[..., None], 0.0).reshape(y.shape)
     code = quantize(z, t.tau)                           # step 3: codebook
+    stored = n
+    if cfg.norm_correction:
+        # the stored norm makes the reconstruction keep the group's norm:
+        # ||(N'/sqrt(L)) c[code]|| = n  <=>  N' = n sqrt(L) / ||c[code]||
+        cg = t.c[code].reshape(yg.shape)
+        stored = n * math.sqrt(L) / np.sqrt(np.sum(cg * cg, axis=-1))
     out = {
         "codes": pack_bits_lsb(code, cfg.bits),         # step 4: packing
-        "norms": fp16_bits(n),
+        "norms": fp16_bits(stored if cfg.norm_group else stored[..., 0]),
         "z": z,
         "code": code,
     }

@@ -40,6 +40,7 @@ import numpy as np
 
 MASK64 = (1 << 64) - 1
 S_STREAM_XOR = 0x514A4C0000000000
+HAAR_STREAM_XOR = 0x4841415200000000
 
 
 def splitmix64(state):
@@ -111,9 +112,40 @@ def gaussian_matrix(seed, m, d):
     Box-Muller on SplitMix64 output pairs, row-major fill (reading above).
     math.log / math.cos / math.sin are the C library's, as in a C host.
     """
+    return _gaussian_stream(seed ^ S_STREAM_XOR, m, d)
+
+
+def haar_rotation(seed, d):
+    """Dense Haar-random rotation Q (d x d, float64), det(Q) = +1.
+
+    The pages' dense alternative to D1.H.D2 ([TQ+ guide] §3: a rotation
+    generated deterministically from a seed by a QR decomposition, with the
+    log-determinant used to force det = +1; §4: the O(d^2) dense rotation
+    beside the fast structured one).  Readings (the pages give no more):
+      * G is d x d from a third SplitMix64 stream seeded with
+        seed XOR 0x4841415200000000, filled row-major by the same
+        Box-Muller pairs as S (entries rounded to float32);
+      * G = Q R (Householder QR in float64), and Q's columns are multiplied
+        by the signs of R's diagonal, which makes Q the unique QR factor with
+        a positive diagonal in R (Haar-distributed for Gaussian G);
+      * if det(Q) = -1, the first column is negated.
+    The rotation is y = Q x, as R x for the structured rotation.
+    """
+    g = _gaussian_stream(seed ^ HAAR_STREAM_XOR, d, d)
+    q, r = np.linalg.qr(g)
+    q = q * np.where(np.diag(r) < 0, -1.0, 1.0)[None, :]
+    sign, _ = np.linalg.slogdet(q)
+    if sign < 0:
+        q[:, 0] = -q[:, 0]
+    return q
+
+
+def _gaussian_stream(stream_seed, m, d):
+    """m x d float32-valued Gaussians from the SplitMix64 stream seeded with
+    stream_seed: Box-Muller on consecutive output pairs, row-major."""
     if (m * d) % 2:
         raise ValueError("m*d must be even")
-    gen = splitmix64(seed ^ S_STREAM_XOR)
+    gen = splitmix64(stream_seed)
     flat = np.empty(m * d, dtype=np.float32)
     two_pi = 2.0 * math.pi
     for k in range(0, m * d, 2):
