@@ -31,7 +31,8 @@
  *   codes  + v * code_bytes   d*b/8 bytes: code i at bits b*i..b*i+b-1 of an
  *                             LSB-first bit stream (bit k is bit k%8 of byte
  *                             k/8); a 32-code block is 4*b bytes
- *   norms  + v                fp16 bits of ||x||_2 (rounded once, RNE)
+ *   norms  + v * nn           fp16 bits of the norms (rounded once, RNE):
+ *                             nn = 1 (||x||_2) or d/32 (block norms of R x)
  *   signs  + v * sign_bytes   QJL: m sign bits, bit l = bit l%8 of byte l/8
  *                             ([Orión plan] Fase 3, sign-bit sketch)
  *   rnorms + v                QJL: fp16 bits of the residual norm gamma
@@ -61,6 +62,13 @@ enum tq_dtype {
     TQ_DTYPE_BF16 = 1,
 };
 
+/* Rotation applied before quantisation ([TQ+ guide] §3, §4: the fast
+ * structured D1.H.D2 rotation and the dense rotation from a seeded QR). */
+enum tq_rotation {
+    TQ_ROTATION_WHT = 0,   /* R = D1.H.D2 / sqrt(d), O(d log d) */
+    TQ_ROTATION_HAAR = 1,  /* R = Q of a seeded Gaussian's QR, det +1, O(d^2) */
+};
+
 /*
  * Method configuration ([TQ+ guide] §5.1-§5.2: MSE-only codebook, block size
  * 32, rotation width decoupled from block size; [Orión plan] Fase 2 settings
@@ -74,6 +82,22 @@ enum tq_dtype {
  *   qjl       1 adds the 1-bit QJL residual sketch ([TQ explainer] §2.2)
  *   qjl_dim   m, rows of S: 0 means m = d (the kernels support only m = d;
  *             another multiple of 32 up to 256 gives TQ_STATUS_UNSUPPORTED)
+ *   rotation  enum tq_rotation.  TQ_ROTATION_HAAR: R = Q with G = Q R' the
+ *             Householder QR of a d x d Gaussian G drawn from the seed (a
+ *             third SplitMix64 stream, seed ^ 0x4841415200000000, Box-Muller
+ *             pairs rounded to float, row-major), Q's columns multiplied by
+ *             the signs of diag(R'), and column 0 negated if det(Q) = -1
+ *             ([TQ+ guide] §3, the seeded QR rotation with det = +1)
+ *   norm_group 0: one fp16 norm per vector (the norm of x); 32: one fp16 norm
+ *             per 32-code block, the norm of that block of the rotated vector
+ *             R x, with z = sqrt(32) (R x)_block / norm_block (the 3.5-bit
+ *             turbo3 layout of [TQ+ guide] §1.2)
+ *   norm_correction 1: the stored norm of each group of L coordinates (the
+ *             vector, L = d, or the block, L = 32) is n sqrt(L) / ||c[code]||
+ *             over the group, so that the reconstruction keeps the group's
+ *             norm ([TQ+ guide] §11 names the method; this is the reading)
+ * QJL contexts take rotation TQ_ROTATION_WHT, norm_group 0 and no correction
+ * (TQ_STATUS_UNSUPPORTED otherwise); a Haar context takes norm_group 0.
  */
 struct tq_config {
     uint64_t seed;
@@ -82,6 +106,9 @@ struct tq_config {
     int32_t block;
     int32_t qjl;
     int32_t qjl_dim;
+    int32_t rotation;
+    int32_t norm_group;
+    int32_t norm_correction;
 };
 
 /* Opaque, immutable context: the config plus its device tables (D1/D2 sign
@@ -119,6 +146,14 @@ int32_t tq_tables_export(const struct tq_config * cfg, int8_t * d1, int8_t * d2,
 /* Bytes per vector in each plane for cfg (0 on an invalid cfg). */
 int64_t tq_code_bytes(const struct tq_config * cfg);
 int64_t tq_sign_bytes(const struct tq_config * cfg);
+/* fp16 norms per vector for cfg: 1, or d/32 with norm_group = 32 (0 on an
+ * invalid cfg). */
+int64_t tq_norm_count(const struct tq_config * cfg);
+
+/* Host-only (no device needed): the dense rotation R (d x d, row-major,
+ * float64) that cfg applies, y = R x: D1.H.D2/sqrt(d) or the Haar Q
+ * ([TQ+ guide] §4).  Errors: INVALID_ARG. */
+int32_t tq_rotation_export(const struct tq_config * cfg, double * r_rowmajor);
 
 /*
  * Encode a [n0, n1, n2] grid of d-vectors ([TQ+ guide] §4, §5.1-§5.2;

@@ -18,9 +18,13 @@ LIB_PATH = os.path.join(_PKG, "libtq.so")
 
 TQ_DTYPE_F32 = 0
 TQ_DTYPE_BF16 = 1
+TQ_ROTATION_WHT = 0
+TQ_ROTATION_HAAR = 1
+_ROTATIONS = {"wht": TQ_ROTATION_WHT, "haar": TQ_ROTATION_HAAR}
 
 EXPORTED = (
-    "tq_ctx_create", "tq_ctx_free", "tq_tables_export", "tq_code_bytes", "tq_sign_bytes",
+    "tq_ctx_create", "tq_ctx_free", "tq_tables_export", "tq_rotation_export", "tq_code_bytes",
+    "tq_sign_bytes", "tq_norm_count",
     "tq_encode", "tq_scores", "tq_scores_workspace", "tq_attend_decode",
     "tq_attend_decode_workspace", "tq_attend_decode_static", "tq_last_error", "tq_version",
 )
@@ -34,7 +38,9 @@ class TQError(RuntimeError):
 
 class Config(ctypes.Structure):
     _fields_ = [("seed", ctypes.c_uint64), ("head_dim", ctypes.c_int32), ("bits", ctypes.c_int32),
-                ("block", ctypes.c_int32), ("qjl", ctypes.c_int32), ("qjl_dim", ctypes.c_int32)]
+                ("block", ctypes.c_int32), ("qjl", ctypes.c_int32), ("qjl_dim", ctypes.c_int32),
+                ("rotation", ctypes.c_int32), ("norm_group", ctypes.c_int32),
+                ("norm_correction", ctypes.c_int32)]
 
 
 class Planes(ctypes.Structure):
@@ -60,6 +66,10 @@ def lib():
         L.tq_ctx_free.restype = None
         L.tq_tables_export.argtypes = [cfgp, vp, vp, vp, vp, vp]
         L.tq_tables_export.restype = i32
+        L.tq_rotation_export.argtypes = [cfgp, vp]
+        L.tq_rotation_export.restype = i32
+        L.tq_norm_count.argtypes = [cfgp]
+        L.tq_norm_count.restype = i64
         L.tq_code_bytes.argtypes = [cfgp]
         L.tq_code_bytes.restype = i64
         L.tq_sign_bytes.argtypes = [cfgp]
@@ -91,8 +101,20 @@ def _check(status):
         raise TQError(status, lib().tq_last_error().decode())
 
 
-def make_config(seed=0, head_dim=128, bits=3, qjl=False, qjl_dim=0, block=32):
-    return Config(seed, head_dim, bits, block, 1 if qjl else 0, qjl_dim)
+def make_config(seed=0, head_dim=128, bits=3, qjl=False, qjl_dim=0, block=32, rotation="wht", norm_group=0,
+                norm_correction=False):
+    rot = _ROTATIONS[rotation] if isinstance(rotation, str) else int(rotation)
+    return Config(seed, head_dim, bits, block, 1 if qjl else 0, qjl_dim, rot, norm_group,
+                  1 if norm_correction else 0)
+
+
+def rotation_export(**cfg_kw):
+    """Host-only: the dense rotation R (d x d float64, y = R x) of a config."""
+    import numpy as np
+    cfg = make_config(**cfg_kw)
+    r = np.zeros((cfg.head_dim, cfg.head_dim), np.float64)
+    _check(lib().tq_rotation_export(ctypes.byref(cfg), r.ctypes.data))
+    return r
 
 
 def tables_export(seed=0, head_dim=128, bits=3, qjl=False, qjl_dim=0):
@@ -127,9 +149,12 @@ def _ptr(t):
 class Context:
     """A libtq context (rotation, codebook and QJL tables on the current GPU)."""
 
-    def __init__(self, seed=0, head_dim=128, bits=3, qjl=False, qjl_dim=0):
-        self.cfg = make_config(seed, head_dim, bits, qjl, qjl_dim)
+    def __init__(self, seed=0, head_dim=128, bits=3, qjl=False, qjl_dim=0, rotation="wht", norm_group=0,
+                 norm_correction=False):
+        self.cfg = make_config(seed, head_dim, bits, qjl, qjl_dim, rotation=rotation, norm_group=norm_group,
+                               norm_correction=norm_correction)
         self.seed, self.head_dim, self.bits, self.qjl = seed, head_dim, bits, bool(qjl)
+        self.rotation, self.norm_group, self.norm_correction = rotation, norm_group, bool(norm_correction)
         self.m = qjl_dim or head_dim
         h = ctypes.c_void_p()
         _check(lib().tq_ctx_create(ctypes.byref(self.cfg), ctypes.byref(h)))
@@ -146,6 +171,11 @@ class Context:
     @property
     def sign_bytes(self):
         return self.m // 8 if self.qjl else 0
+
+    @property
+    def norm_count(self):
+        """fp16 norms per vector: 1, or head_dim / 32 with block norms."""
+        return self.head_dim // self.norm_group if self.norm_group else 1
 
     def close(self):
         if getattr(self, "_h", None):
@@ -166,14 +196,16 @@ class Context:
 @dataclass
 class PackedPlanes:
     codes: torch.Tensor    # u8 [..., code_bytes]
-    norms: torch.Tensor    # int16 (fp16 bits) [...]
+    norms: torch.Tensor    # int16 (fp16 bits) [...], or [..., d/32] with block norms
     signs: torch.Tensor    # u8 [..., sign_bytes] or None
     rnorms: torch.Tensor   # int16 [...] or None
 
     @staticmethod
     def empty(ctx, shape, device):
         codes = torch.empty(shape + (ctx.code_bytes,), dtype=torch.uint8, device=device)
-        norms = torch.empty(shape, dtype=torch.int16, device=device)
+        nc = getattr(ctx, "norm_count", 1)
+        norms = torch.empty(shape + ((nc,) if getattr(ctx, "norm_group", 0) else ()), dtype=torch.int16,
+                            device=device)
         signs = rnorms = None
         if ctx.qjl:
             signs = torch.empty(shape + (ctx.sign_bytes,), dtype=torch.uint8, device=device)
@@ -182,20 +214,31 @@ class PackedPlanes:
 
     @property
     def grid(self):
-        return tuple(self.norms.shape)
+        return tuple(self.codes.shape[:-1])
+
+    @property
+    def block_norms(self):
+        """True when the norms plane holds one norm per 32-code block."""
+        return self.norms.dim() == self.codes.dim()
 
     def c_struct(self):
-        """Planes struct; strides in vectors from the norms tensor (3-D grid, padded in front).
-        Every plane must share the norms' vector layout (its per-vector
-        bytes contiguous), since the C ABI carries one set of strides."""
-        st = list(self.norms.stride())
-        for name, t in (("codes", self.codes), ("signs", self.signs), ("rnorms", self.rnorms)):
+        """Planes struct; strides in vectors (3-D grid, padded in front).
+        Every plane must share one vector layout (each vector's bytes of a
+        plane contiguous), since the C ABI carries one set of strides: they
+        are taken from the codes plane and checked against the others."""
+        cb = self.codes.shape[-1]
+        if self.codes.stride(-1) != 1 or any(x % cb for x in self.codes.stride()[:-1]):
+            raise ValueError("codes plane: each vector's code bytes must be contiguous")
+        st = [x // cb for x in self.codes.stride()[:-1]]
+        for name, t in (("norms", self.norms), ("signs", self.signs), ("rnorms", self.rnorms)):
             if t is None:
                 continue
-            per = t.shape[-1] if name in ("codes", "signs") else 1
-            lead = list(t.stride())[:-1] if name in ("codes", "signs") else list(t.stride())
-            if (name in ("codes", "signs") and t.stride(-1) != 1) or lead != [x * per for x in st]:
-                raise ValueError(f"{name} plane layout does not match the norms plane's vector strides")
+            per_vec = name == "signs" or (name == "norms" and self.block_norms)
+            per = t.shape[-1] if per_vec else 1
+            lead = list(t.stride())[:-1] if per_vec else list(t.stride())
+            if (per_vec and t.stride(-1) != 1) or lead != [x * per for x in st] or \
+                    tuple(t.shape[:len(st)]) != self.grid:
+                raise ValueError(f"{name} plane layout does not match the codes plane's vector strides")
         st = [0] * (3 - len(st)) + st
         p = Planes()
         p.codes = self.codes.data_ptr()
@@ -245,6 +288,7 @@ def encode(ctx: Context, x: torch.Tensor, planes: PackedPlanes = None, stream=No
         planes = ctx.new_planes(grid, x.device)
     if tuple(planes.grid) != grid:
         raise ValueError("planes grid does not match x")
+    _check_planes(planes, ctx, grid, "out")
     n = [1] * (3 - len(grid)) + list(grid)
     xs = [0] * (3 - len(grid)) + list(x.stride()[:-1])
     xs_arr = (ctypes.c_int64 * 3)(*xs)
@@ -272,6 +316,10 @@ def _check_query(q, ctx, ndim, what="q"):
 def _check_planes(p, ctx, grid_prefix, what):
     if p.codes.shape[-1] != ctx.code_bytes or tuple(p.codes.shape[:-1]) != tuple(p.grid):
         raise ValueError(f"{what} planes do not match the context's code bytes per vector")
+    nc = getattr(ctx, "norm_count", 1)
+    want = tuple(p.grid) + ((nc,) if getattr(ctx, "norm_group", 0) else ())
+    if tuple(p.norms.shape) != want:
+        raise ValueError(f"{what} norms plane has shape {tuple(p.norms.shape)}, the context needs {want}")
     if ctx.qjl and (p.signs is None or p.rnorms is None or p.signs.shape[-1] != ctx.sign_bytes):
         raise ValueError(f"{what} planes lack the QJL sign/rnorm planes of the context")
     if tuple(p.grid[:len(grid_prefix)]) != tuple(grid_prefix):

@@ -262,10 +262,13 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     // codes are in flight while the queries and tables are set up (NS
     // register sets: the steps NS - 1 ahead are in flight while one is
     // processed).
+    // (a dense-rotation context has its queries rotated by the query kernel
+    // beforehand: they are read from the prepared rows instead)
     float4 qv0 = {0.f, 0.f, 0.f, 0.f}, qv1 = {0.f, 0.f, 0.f, 0.f};
     if (wave == 0) {
-        const float4 * src = reinterpret_cast<const float4 *>(a.q + (int64_t(b) * a.Hq + g * kG + (lane >> 4)) * kD +
-                                                              8 * (lane & 15));
+        const int64_t qrow = int64_t(b) * a.Hq + g * kG + (lane >> 4);
+        const float4 * src = reinterpret_cast<const float4 *>(
+            (kt.haar ? a.qp + qrow * a.qp_stride : a.q + qrow * kD) + 8 * (lane & 15));
         qv0 = src[0];
         qv1 = src[1];
     }
@@ -305,7 +308,12 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     // 8(l%16)..+7 of head l/16; three butterfly stages run in registers, four
     // across the 16 lanes of the head.  For QJL keys the four waves then form
     // S q' (rows 32 w .. 32 w + 31, two lanes per row).
-    if (wave == 0) {
+    if (wave == 0 && kt.haar) {
+        const int h = lane >> 4, e0 = 8 * (lane & 15);
+        float4 * dst = reinterpret_cast<float4 *>(qst + h * 2 * kD + e0);
+        dst[0] = qv0;
+        dst[1] = qv1;
+    } else if (wave == 0) {
         const int h = lane >> 4, e0 = 8 * (lane & 15);
         float v[8] = {qv0.x, qv0.y, qv0.z, qv0.w, qv1.x, qv1.y, qv1.z, qv1.w};
         // sign words picked from the (uniform) four words by selects: a
@@ -685,7 +693,10 @@ int attend_mfma_blocks_per_cu(const dev_tables & kt, const dev_tables & vt) {
 int attend_mfma_chunk_quantum() { return 4 * kStep; }
 
 bool attend_mfma_shape_ok(const dev_tables & kt, const dev_tables & vt, int32_t Hq, int32_t Hkv) {
-    return kt.d == kD && vt.d == kD && Hq == kG * Hkv && (!kt.qjl || kt.m == kD);
+    // one norm per vector (block norms take the general kernel); a dense
+    // rotation only with MSE-only keys (its queries come prepared)
+    return kt.d == kD && vt.d == kD && Hq == kG * Hkv && (!kt.qjl || kt.m == kD) && !kt.norm_group &&
+           !vt.norm_group && (!kt.haar || !kt.qjl);
 }
 
 bool attend_mfma_supported(const dev_tables & kt, const dev_tables & vt, const attend_args & a) {

@@ -42,12 +42,27 @@ __global__ __launch_bounds__(256) void query_prep_kernel(const dev_tables t, con
     __shared__ float s[D];
     const int64_t i = blockIdx.x;
     const int k = threadIdx.x;
-    float x = q[i * D + k];
-    if ((t.d2[k >> 5] >> (k & 31)) & 1) x = -x;
-    s[k] = x;
-    lds_fwht<D>(s, k);
-    float y = s[k] * (1.0f / sqrtf(static_cast<float>(D)));
-    if ((t.d1[k >> 5] >> (k & 31)) & 1) y = -y;
+    float y;
+    if (t.haar) {
+        // dense rotation: q'_k = sum_j Q_kj q_j ([TQ+ guide] §4, the O(d^2) form)
+        s[k] = q[i * D + k];
+        __syncthreads();
+        const float4 * row = reinterpret_cast<const float4 *>(t.Q + int64_t(k) * D);
+        float acc = 0.f;
+#pragma unroll 4
+        for (int j = 0; j < D / 4; ++j) {
+            const float4 r = row[j];
+            acc = fmaf(r.x, s[4 * j], fmaf(r.y, s[4 * j + 1], fmaf(r.z, s[4 * j + 2], fmaf(r.w, s[4 * j + 3], acc))));
+        }
+        y = acc;
+    } else {
+        float x = q[i * D + k];
+        if ((t.d2[k >> 5] >> (k & 31)) & 1) x = -x;
+        s[k] = x;
+        lds_fwht<D>(s, k);
+        y = s[k] * (1.0f / sqrtf(static_cast<float>(D)));
+        if ((t.d1[k >> 5] >> (k & 31)) & 1) y = -y;
+    }
     qp[i * stride + k] = y;
     if constexpr (QJL) {
         __syncthreads();
@@ -70,6 +85,7 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(const dev_tables kt
     __shared__ __align__(16) float us[QJL ? D : 1][QJL ? G : 1];
     __shared__ __align__(16) float sc[kSub][G];
     __shared__ uint32_t vcode[kSub][VW + 1];
+    __shared__ float vnb[kSub][D / 32 + 1];   // value block norms (norm_group 32)
     __shared__ float cbk[16], cbv[16];
     __shared__ float red[4][G];
     __shared__ float accred[PARTS][G][D];
@@ -103,6 +119,11 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(const dev_tables kt
     }
     const float inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(D));
     const float qjl_coef = QJL ? sqrtf(0.5f * static_cast<float>(M_PI)) / static_cast<float>(D) : 0.f;
+    // one norm per 32-code block (norm_group 32): block b of a key scores
+    // (N_b / sqrt(32)) <q'_b, c[code_b]>, and a value block is scaled alike
+    const bool kbn = kt.norm_group != 0, vbn = vt.norm_group != 0;
+    const float k_inv_len = kbn ? 1.0f / sqrtf(32.f) : inv_sqrt_d;
+    const float v_inv_len = vbn ? 1.0f / sqrtf(32.f) : inv_sqrt_d;
     const int64_t kb = int64_t(b) * a.k.stride[0] + int64_t(g) * a.k.stride[1];
     const int64_t vb = int64_t(b) * a.v.stride[0] + int64_t(g) * a.v.stride[1];
     __syncthreads();
@@ -123,14 +144,20 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(const dev_tables kt
                 uint32_t w[KB];
 #pragma unroll
                 for (int k = 0; k < KB; ++k) w[k] = crow[bl * KB + k];
+                float bd[G];
+#pragma unroll
+                for (int h = 0; h < G; ++h) bd[h] = 0.f;
 #pragma unroll
                 for (int i = 0; i < 32; ++i) {
                     const float cv = cbk[block_code<KB>(w, i)];
 #pragma unroll
-                    for (int h = 0; h < G; ++h) dot[h] = fmaf(qs[bl * 32 + i][h], cv, dot[h]);
+                    for (int h = 0; h < G; ++h) bd[h] = fmaf(qs[bl * 32 + i][h], cv, bd[h]);
                 }
+                const float wb = kbn ? half_bits_to_float(a.k.norms[kv * (D / 32) + bl]) : 1.f;
+#pragma unroll
+                for (int h = 0; h < G; ++h) dot[h] = fmaf(wb, bd[h], dot[h]);
             }
-            const float nk = half_bits_to_float(a.k.norms[kv]);
+            const float nk = kbn ? 1.f : half_bits_to_float(a.k.norms[kv]);
             if constexpr (QJL) {
                 const uint32_t * srow = reinterpret_cast<const uint32_t *>(a.k.signs + kv * (D / 8));
                 float dq[G];
@@ -152,10 +179,16 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(const dev_tables kt
                     s[h] = a.scale * nk * (dot[h] * inv_sqrt_d + gam * qjl_coef * dq[h]);
             } else {
 #pragma unroll
-                for (int h = 0; h < G; ++h) s[h] = a.scale * nk * inv_sqrt_d * dot[h];
+                for (int h = 0; h < G; ++h) s[h] = a.scale * nk * k_inv_len * dot[h];
             }
             const int64_t vv = vb + j * a.v.stride[2];
-            wv_norm = half_bits_to_float(a.v.norms[vv]) * inv_sqrt_d;
+            if (vbn) {
+                wv_norm = v_inv_len;
+#pragma unroll
+                for (int bl = 0; bl < D / 32; ++bl) vnb[tid][bl] = half_bits_to_float(a.v.norms[vv * (D / 32) + bl]);
+            } else {
+                wv_norm = half_bits_to_float(a.v.norms[vv]) * inv_sqrt_d;
+            }
             const uint32_t * vrow = reinterpret_cast<const uint32_t *>(a.v.codes + vv * (D * VB / 8));
 #pragma unroll
             for (int k = 0; k < VW; ++k) vcode[tid][k] = vrow[k];
@@ -164,6 +197,12 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(const dev_tables kt
             for (int h = 0; h < G; ++h) s[h] = -INFINITY;
 #pragma unroll
             for (int k = 0; k < VW; ++k) vcode[tid][k] = 0;
+            // a slot past the length has weight 0; its block norms must be
+            // finite too (0 * NaN from stale LDS would poison the sums)
+            if (vbn) {
+#pragma unroll
+                for (int bl = 0; bl < D / 32; ++bl) vnb[tid][bl] = 0.f;
+            }
         }
         // sub-tile max per head
 #pragma unroll
@@ -198,7 +237,7 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(const dev_tables kt
         for (int jj = part; jj < kSub; jj += PARTS) {
             uint32_t c = vcode[jj][wi] >> off;
             if (off + VB > 32) c |= vcode[jj][wi + 1] << (32 - off);
-            const float cv = cbv[c & ((1u << VB) - 1)];
+            const float cv = vbn ? cbv[c & ((1u << VB) - 1)] * vnb[jj][e_dim >> 5] : cbv[c & ((1u << VB) - 1)];
 #pragma unroll
             for (int h = 0; h < G; ++h) pv[h] = fmaf(sc[jj][h], cv, pv[h]);
         }
@@ -254,6 +293,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(const dev_tables vt, 
     constexpr int CB = 16;                     // chunks per wave per batch
     __shared__ float wm[4], wl[4];
     __shared__ float wacc[4][PER * 64];
+    __shared__ float ost[D];  // normalised rotated-domain output (dense rotation)
     const int h = blockIdx.x, b = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -308,6 +348,31 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(const dev_tables vt, 
     }
     const bool ok = Mx != -INFINITY && L > 0.f;
     const float inv = ok ? 1.0f / L : 0.f;
+    if (vt.haar) {
+        // dense rotation: o = Q^T o'  ([TQ+ guide] §6.1, rotated back with
+        // the value context's rotation); o' staged in LDS, column reads of Q
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int dim = lane + 64 * i;
+            if (dim < D) {
+                float o = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) o = fmaf(sw[w], wacc[w][dim], o);
+                ost[dim] = o * inv;
+            }
+        }
+        __threadfence_block();  // this wave's LDS writes land before its reads
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int dim = lane + 64 * i;
+            if (dim < D) {
+                float o = 0.f;
+                for (int j = 0; j < D; ++j) o = fmaf(vt.Q[int64_t(j) * D + dim], ost[j], o);
+                a.out[(int64_t(b) * a.Hq + h) * D + dim] = o;
+            }
+        }
+        return;
+    }
     float x[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -355,8 +420,8 @@ hipError_t launch_attend_g(const dev_tables & kt, const dev_tables & vt, const a
                            hipStream_t s) {
     const dim3 grid(a.n_chunks, a.Hkv, a.B);
     const bool mfma = attend_mfma_supported(kt, vt, a);
-    // the matrix-core kernel prepares its queries itself
-    if (!mfma) {
+    // the matrix-core kernel rotates its queries itself (D1.H.D2 contexts)
+    if (!mfma || kt.haar) {
         hipError_t e = launch_query_prep(kt, a.q, int64_t(a.B) * a.Hq, a.qp, a.qp_stride, s);
         if (e != hipSuccess) return e;
     }

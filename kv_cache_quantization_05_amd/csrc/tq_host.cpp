@@ -12,6 +12,7 @@ struct tq_ctx {
     int device;
     tq::dev_tables tab;
     float * S_dev;
+    float * Q_dev;
 };
 
 namespace {
@@ -98,6 +99,21 @@ int64_t tq_sign_bytes(const tq_config * cfg) {
     return cfg->qjl ? m_of(*cfg) / 8 : 0;
 }
 
+int64_t tq_norm_count(const tq_config * cfg) {
+    const char * why;
+    if (!cfg || tq::validate_config(*cfg, &why) == TQ_STATUS_INVALID_ARG) return 0;
+    return cfg->norm_group ? cfg->head_dim / cfg->norm_group : 1;
+}
+
+int32_t tq_rotation_export(const tq_config * cfg, double * r_rowmajor) {
+    if (!cfg || !r_rowmajor) return fail(TQ_STATUS_INVALID_ARG, "cfg and r_rowmajor must be non-NULL");
+    const char * why = "";
+    int32_t st = tq::validate_config(*cfg, &why);
+    if (st == TQ_STATUS_INVALID_ARG) return fail(st, "invalid config: %s", why);
+    tq::build_rotation(*cfg, r_rowmajor);
+    return ok();
+}
+
 int32_t tq_tables_export(const tq_config * cfg, int8_t * d1, int8_t * d2, float * codebook,
                          float * thresholds, float * s_rowmajor) {
     if (!cfg) return fail(TQ_STATUS_INVALID_ARG, "cfg is NULL");
@@ -143,7 +159,42 @@ int32_t tq_ctx_create(const tq_config * cfg, tq_ctx ** out) {
     c->tab.bits = cfg->bits;
     c->tab.m = static_cast<int32_t>(m);
     c->tab.qjl = cfg->qjl;
+    c->tab.haar = cfg->rotation == TQ_ROTATION_HAAR;
+    c->tab.norm_group = cfg->norm_group;
+    c->tab.norm_corr = cfg->norm_correction;
     c->tab.S = nullptr;
+    c->tab.Q = nullptr;
+    c->Q_dev = nullptr;
+    if (c->tab.haar) {
+        // one allocation: Q (fp32), then the fp16 split of 16 Q (hi, lo):
+        // the scale keeps the low parts of the small entries normal in fp16
+        const size_t n = size_t(d) * d;
+        std::vector<double> qd(n);
+        tq::build_rotation(*cfg, qd.data());
+        std::vector<float> qf(n), q16(n);
+        for (size_t i = 0; i < n; ++i) {
+            qf[i] = static_cast<float>(qd[i]);
+            q16[i] = static_cast<float>(16.0 * qd[i]);
+        }
+        std::vector<uint16_t> h16(2 * n);
+        tq::split_fp16(q16.data(), static_cast<int64_t>(n), h16.data(), h16.data() + n);
+        const size_t bytes = n * sizeof(float) + 2 * n * sizeof(uint16_t);
+        hipError_t e = hipMalloc(&c->Q_dev, bytes);
+        if (e != hipSuccess) {
+            delete c;
+            return fail(TQ_STATUS_NO_MEMORY, "hipMalloc of the rotation failed: %s", hipGetErrorString(e));
+        }
+        e = hipMemcpy(c->Q_dev, qf.data(), n * sizeof(float), hipMemcpyHostToDevice);
+        if (e == hipSuccess)
+            e = hipMemcpy(c->Q_dev + n, h16.data(), 2 * n * sizeof(uint16_t), hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            hipFree(c->Q_dev);
+            delete c;
+            return device_status(e, "upload of the rotation");
+        }
+        c->tab.Q = c->Q_dev;
+        c->tab.Q16 = reinterpret_cast<const uint16_t *>(c->Q_dev + n);
+    }
     if (cfg->qjl) {
         // one allocation: S (fp32), then its fp16 split hi and lo
         const size_t n = S.size();
@@ -152,6 +203,7 @@ int32_t tq_ctx_create(const tq_config * cfg, tq_ctx ** out) {
         const size_t bytes = n * sizeof(float) + 2 * n * sizeof(uint16_t);
         hipError_t e = hipMalloc(&c->S_dev, bytes);
         if (e != hipSuccess) {
+            if (c->Q_dev) hipFree(c->Q_dev);
             delete c;
             return fail(TQ_STATUS_NO_MEMORY, "hipMalloc of S failed: %s", hipGetErrorString(e));
         }
@@ -160,6 +212,7 @@ int32_t tq_ctx_create(const tq_config * cfg, tq_ctx ** out) {
             e = hipMemcpy(c->S_dev + n, s16.data(), 2 * n * sizeof(uint16_t), hipMemcpyHostToDevice);
         if (e != hipSuccess) {
             hipFree(c->S_dev);
+            if (c->Q_dev) hipFree(c->Q_dev);
             delete c;
             return device_status(e, "upload of S");
         }
@@ -173,6 +226,7 @@ int32_t tq_ctx_create(const tq_config * cfg, tq_ctx ** out) {
 void tq_ctx_free(tq_ctx * ctx) {
     if (!ctx) return;
     if (ctx->S_dev) hipFree(ctx->S_dev);
+    if (ctx->Q_dev) hipFree(ctx->Q_dev);
     delete ctx;
 }
 
@@ -204,7 +258,7 @@ int64_t tq_scores_workspace(const tq_ctx * k_ctx, int64_t n_q, int64_t n_k, int3
     if (top_k == 0) return qp;
     int32_t ranges = 1;
     int64_t per = 0;
-    tq::scores_plan(k_ctx->tab.d, n_q, n_k, ranges, per);
+    tq::scores_plan(k_ctx->tab.d, k_ctx->tab.norm_group != 0, n_q, n_k, ranges, per);
     return qp + round_up(int64_t(ranges) * n_q * top_k * 4) + round_up(int64_t(ranges) * n_q * top_k * 8);
 }
 
@@ -241,7 +295,7 @@ int32_t tq_scores(const tq_ctx * k_ctx, const float * q, int64_t n_q, float scal
     a.top_k = top_k;
     a.out_scores = out_scores;
     a.out_idx = out_idx;
-    tq::scores_plan(k_ctx->tab.d, n_q, n_k, a.n_ranges, a.keys_per_range);
+    tq::scores_plan(k_ctx->tab.d, k_ctx->tab.norm_group != 0, n_q, n_k, a.n_ranges, a.keys_per_range);
     if (top_k > 0) {
         char * p = ws + round_up(n_q * qp_stride * 4);
         a.cand_s = reinterpret_cast<float *>(p);
@@ -268,8 +322,8 @@ int32_t tq_attend_decode(const tq_ctx * k_ctx, const tq_ctx * v_ctx, const float
     if (!k_ctx || !v_ctx) return fail(TQ_STATUS_INVALID_ARG, "k_ctx and v_ctx must be non-NULL");
     if (k_ctx->tab.d != v_ctx->tab.d)
         return fail(TQ_STATUS_INVALID_ARG, "k_ctx and v_ctx must share head_dim");
-    if (k_ctx->cfg.seed != v_ctx->cfg.seed)
-        return fail(TQ_STATUS_UNSUPPORTED, "k_ctx and v_ctx must share the rotation seed");
+    if (k_ctx->cfg.seed != v_ctx->cfg.seed || k_ctx->cfg.rotation != v_ctx->cfg.rotation)
+        return fail(TQ_STATUS_UNSUPPORTED, "k_ctx and v_ctx must share the rotation (seed and kind)");
     if (v_ctx->cfg.qjl) return fail(TQ_STATUS_INVALID_ARG, "v_ctx must not use QJL");
     if (k_ctx->device != v_ctx->device) return fail(TQ_STATUS_INVALID_ARG, "contexts on different devices");
     if (B < 0 || Hq < 0 || Hkv <= 0 || t_max < 0) return fail(TQ_STATUS_INVALID_ARG, "negative sizes");

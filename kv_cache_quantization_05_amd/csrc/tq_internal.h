@@ -29,16 +29,26 @@ struct dev_tables {
     float th[16];        // 2^b - 1 thresholds; th[2^b - 1 ..] = +inf
     const float * S;     // device, m x d row-major (QJL only)
     const uint16_t * S16;  // device, fp16 split of S: hi [m x d] then lo [m x d]
+    const float * Q;     // device, d x d row-major dense rotation (Haar only), y = Q x
+    const uint16_t * Q16;  // device, fp16 split of 16 Q: hi [d x d] then lo [d x d]
     int32_t d;
     int32_t bits;
     int32_t m;
     int32_t qjl;
+    int32_t haar;        // rotation is the dense Q (else D1.H.D2)
+    int32_t norm_group;  // 0: one norm per vector; 32: one per 32-code block
+    int32_t norm_corr;   // stored norms carry the norm correction
 };
+
+// Norms per vector in the norms plane.
+inline int norms_per_vector(const dev_tables & t) { return t.norm_group ? t.d / t.norm_group : 1; }
 
 // Host-side table generation (tq_tables.cpp); independent of any device.
 int build_tables(const tq_config & cfg, int8_t * d1, int8_t * d2, float * codebook,
                  float * thresholds, float * s_rowmajor);
 int validate_config(const tq_config & cfg, const char ** why);
+// Dense rotation R (d x d row-major float64): y = R x.
+void build_rotation(const tq_config & cfg, double * r);
 // hi = fp16(v), lo = fp16(v - hi), both round-to-nearest-even (v ~ hi + lo
 // to ~2^-22 relative).
 void split_fp16(const float * v, int64_t n, uint16_t * hi, uint16_t * lo);
@@ -52,6 +62,8 @@ struct encode_args {
     tq_planes out;
 };
 hipError_t launch_encode(const dev_tables & t, const encode_args & a, hipStream_t s);
+// Haar rotation, block norms or norm correction (tq_encode_var.hip).
+hipError_t launch_encode_variant(const dev_tables & t, const encode_args & a, hipStream_t s);
 bool encode_grid_supported(const encode_args & a);  // n0*n1*n2 < 2^32
 
 // Query preparation: qp[i] = [ R q_i (d floats) | S R q_i (m floats, qjl) ].
@@ -102,6 +114,6 @@ struct scores_args {
 };
 hipError_t launch_scores(const dev_tables & t, const scores_args & a, hipStream_t s);
 // Split of the keys into ranges (one block column each) for head_dim d.
-void scores_plan(int d, int64_t n_q, int64_t n_k, int32_t & ranges, int64_t & keys_per_range);
+void scores_plan(int d, bool block_norms, int64_t n_q, int64_t n_k, int32_t & ranges, int64_t & keys_per_range);
 
 }  // namespace tq

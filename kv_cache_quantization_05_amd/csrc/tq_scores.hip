@@ -29,20 +29,29 @@ __device__ __forceinline__ void score_key(const dev_tables & t, const scores_arg
     float dot[kQT];
 #pragma unroll
     for (int i = 0; i < kQT; ++i) dot[i] = 0.f;
+    // one norm per 32-code block (norm_group 32): block b weighs in with
+    // N_b / sqrt(32) instead of one N / sqrt(d)
+    const bool bn = t.norm_group != 0;
 #pragma unroll 1
     for (int bl = 0; bl < D / 32; ++bl) {
         uint32_t w[KB];
 #pragma unroll
         for (int k = 0; k < KB; ++k) w[k] = crow[bl * KB + k];
+        float bd[kQT];
+#pragma unroll
+        for (int i = 0; i < kQT; ++i) bd[i] = 0.f;
 #pragma unroll
         for (int e = 0; e < 32; ++e) {
             const float cv = cb[block_code<KB>(w, e)];
 #pragma unroll
-            for (int i = 0; i < kQT; ++i) dot[i] = fmaf(qs[bl * 32 + e][i], cv, dot[i]);
+            for (int i = 0; i < kQT; ++i) bd[i] = fmaf(qs[bl * 32 + e][i], cv, bd[i]);
         }
+        const float wb = bn ? half_bits_to_float(a.k.norms[kv * (D / 32) + bl]) : 1.f;
+#pragma unroll
+        for (int i = 0; i < kQT; ++i) dot[i] = fmaf(wb, bd[i], dot[i]);
     }
-    const float n = half_bits_to_float(a.k.norms[kv]);
-    const float inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(D));
+    const float n = bn ? 1.f : half_bits_to_float(a.k.norms[kv]);
+    const float inv_sqrt_d = bn ? 1.0f / sqrtf(32.f) : 1.0f / sqrtf(static_cast<float>(D));
     if constexpr (QJL) {
         const uint32_t * srow = reinterpret_cast<const uint32_t *>(a.k.signs + kv * (D / 8));
         float dq[kQT];
@@ -66,7 +75,6 @@ __device__ __forceinline__ void score_key(const dev_tables & t, const scores_arg
 #pragma unroll
         for (int i = 0; i < kQT; ++i) out[i] = a.scale * n * inv_sqrt_d * dot[i];
     }
-    (void)t;
 }
 
 template <int D, bool QJL>
@@ -469,17 +477,19 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(const dev_tables t, co
 template <int D, int KB, bool QJL>
 hipError_t launch_scores_t(const dev_tables & t, const scores_args & a, hipStream_t s) {
     if constexpr (D >= 128) {
-        const int64_t items = ((a.n_q + 15) / 16 + 3) / 4 * a.n_ranges;
-        const dim3 grid(static_cast<uint32_t>((items + 7) / 8 * 8));
-        if (a.top_k == 0) {
-            hipLaunchKernelGGL((scores_mfma_kernel<D, KB, QJL, false>), grid, dim3(256), 0, s, t, a);
+        if (!t.norm_group) {
+            const int64_t items = ((a.n_q + 15) / 16 + 3) / 4 * a.n_ranges;
+            const dim3 grid(static_cast<uint32_t>((items + 7) / 8 * 8));
+            if (a.top_k == 0) {
+                hipLaunchKernelGGL((scores_mfma_kernel<D, KB, QJL, false>), grid, dim3(256), 0, s, t, a);
+                return hipGetLastError();
+            }
+            hipLaunchKernelGGL((scores_mfma_kernel<D, KB, QJL, true>), grid, dim3(256), 0, s, t, a);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(topk_merge_kernel, dim3(a.n_q), dim3(64), 0, s, a);
             return hipGetLastError();
         }
-        hipLaunchKernelGGL((scores_mfma_kernel<D, KB, QJL, true>), grid, dim3(256), 0, s, t, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(topk_merge_kernel, dim3(a.n_q), dim3(64), 0, s, a);
-        return hipGetLastError();
     }
     const int64_t qtiles = (a.n_q + kQT - 1) / kQT;
     if (a.top_k == 0) {
@@ -510,12 +520,12 @@ hipError_t launch_scores_d(const dev_tables & t, const scores_args & a, hipStrea
 
 }  // namespace
 
-// Matrix-core path (d >= 128): about 4096 waves in all (one per 16 queries
+// Matrix-core path (d >= 128, one norm per vector): about 4096 waves in all (one per 16 queries
 // and range), at most 256 ranges (the final merge reads up to 4 lists per
 // lane), ranges a multiple of 16 keys.  VALU path: ranges of ~4096 keys.
-void scores_plan(int d, int64_t n_q, int64_t n_k, int32_t & ranges, int64_t & keys_per_range) {
+void scores_plan(int d, bool block_norms, int64_t n_q, int64_t n_k, int32_t & ranges, int64_t & keys_per_range) {
     int64_t r;
-    if (d >= 128) {
+    if (d >= 128 && !block_norms) {
         const int64_t qtiles = (n_q + 15) / 16;
         r = (4096 + qtiles - 1) / qtiles;
         const int64_t max_r = (n_k + 15) / 16;

@@ -9,6 +9,9 @@
 //     config seed; the entry is -1 when the output's top bit is set;
 //   * S (m x d, row-major) from the stream seeded with seed ^ 0x514A4C00...;
 //     consecutive output pairs -> Box-Muller (double) -> two float entries;
+//   * the dense Haar rotation from a third stream (seed ^ 0x48414152...),
+//     the same Box-Muller fill, and a Householder QR with the sign and
+//     determinant fixes ([TQ+ guide] §3: QR of a seeded matrix, det = +1);
 //   * codebook: Lloyd-Max quantiser of N(0,1) with 2^b levels (Max 1960),
 //     each centroid rounded once from double to fp16 (RNE); thresholds are
 //     midpoints of neighbouring fp16 centroids (exact in float).
@@ -23,6 +26,7 @@ namespace {
 
 constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
 constexpr uint64_t kSStream = 0x514A4C0000000000ull;
+constexpr uint64_t kHaarStream = 0x4841415200000000ull;
 
 uint64_t mix64(uint64_t z) {
     z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
@@ -53,6 +57,18 @@ uint16_t half_bits_from_double(double v) {
     }
     if (e + 15 >= 31) return sign | 0x7C00;
     return sign | static_cast<uint16_t>(((e + 15) << 10) | (static_cast<int>(q) - 1024));
+}
+
+// Outputs k, k + 1 of the stream seeded with `stream` -> two Gaussians
+// (Box-Muller in double, each rounded to float).
+void box_muller(uint64_t stream, int64_t k, float & g0, float & g1) {
+    const uint64_t z1 = splitmix_at(stream, k);
+    const uint64_t z2 = splitmix_at(stream, k + 1);
+    const double u1 = std::ldexp(static_cast<double>((z1 >> 11) + 1), -53);
+    const double u2 = std::ldexp(static_cast<double>(z2 >> 11), -53);
+    const double r = std::sqrt(-2.0 * std::log(u1));
+    g0 = static_cast<float>(r * std::cos(2.0 * M_PI * u2));
+    g1 = static_cast<float>(r * std::sin(2.0 * M_PI * u2));
 }
 
 double half_bits_to_double(uint16_t h) {
@@ -126,11 +142,120 @@ int validate_config(const tq_config & cfg, const char ** why) {
         *why = "qjl_dim must be 0 or a multiple of 32 up to 256";
         return TQ_STATUS_INVALID_ARG;
     }
+    if (cfg.rotation != TQ_ROTATION_WHT && cfg.rotation != TQ_ROTATION_HAAR) {
+        *why = "rotation must be TQ_ROTATION_WHT or TQ_ROTATION_HAAR";
+        return TQ_STATUS_INVALID_ARG;
+    }
+    if (cfg.norm_group != 0 && cfg.norm_group != 32) {
+        *why = "norm_group must be 0 (one norm per vector) or 32 (one per 32-code block)";
+        return TQ_STATUS_INVALID_ARG;
+    }
+    if (cfg.norm_correction != 0 && cfg.norm_correction != 1) {
+        *why = "norm_correction must be 0 or 1";
+        return TQ_STATUS_INVALID_ARG;
+    }
+    if (cfg.qjl && (cfg.norm_group != 0 || cfg.norm_correction != 0)) {
+        *why = "QJL keys take one plain norm per vector (norm_group 0, no correction)";
+        return TQ_STATUS_INVALID_ARG;
+    }
     if (cfg.qjl && cfg.qjl_dim != 0 && cfg.qjl_dim != d) {
         *why = "qjl_dim other than head_dim is not supported by the kernels";
         return TQ_STATUS_UNSUPPORTED;
     }
+    if (cfg.qjl && cfg.rotation == TQ_ROTATION_HAAR) {
+        *why = "QJL keys with the Haar rotation are not supported by the kernels";
+        return TQ_STATUS_UNSUPPORTED;
+    }
+    if (cfg.rotation == TQ_ROTATION_HAAR && cfg.norm_group != 0) {
+        *why = "block norms with the Haar rotation are not supported by the kernels";
+        return TQ_STATUS_UNSUPPORTED;
+    }
     return TQ_STATUS_OK;
+}
+
+// Dense rotation R (d x d, row-major) applied as y = R x.
+//  * WHT: R = D1 H D2 / sqrt(d), H the Sylvester matrix (+-1 / sqrt(d)).
+//  * Haar: Householder QR of the seeded Gaussian G (stream seed ^ "HAAR",
+//    Box-Muller pairs as for S, entries rounded to float), then Q's columns
+//    times the signs of R's diagonal (the unique factor with a positive
+//    diagonal), then column 0 negated if det(Q) = -1.
+void build_rotation(const tq_config & cfg, double * r) {
+    const int d = cfg.head_dim;
+    if (cfg.rotation != TQ_ROTATION_HAAR) {
+        std::vector<int8_t> d1(d), d2(d);
+        build_tables(cfg, d1.data(), d2.data(), nullptr, nullptr, nullptr);
+        const double s = 1.0 / std::sqrt(static_cast<double>(d));
+        for (int i = 0; i < d; ++i)
+            for (int j = 0; j < d; ++j)
+                r[int64_t(i) * d + j] = ((__builtin_popcount(i & j) & 1) ? -s : s) * d1[i] * d2[j];
+        return;
+    }
+    std::vector<double> a(int64_t(d) * d);
+    {
+        const uint64_t gs = cfg.seed ^ kHaarStream;
+        for (int64_t k = 0; k < int64_t(d) * d; k += 2) {
+            float g0, g1;
+            box_muller(gs, k, g0, g1);
+            a[k] = g0;
+            a[k + 1] = g1;
+        }
+    }
+    // Householder: column k's reflector v_k (unit) maps a[k:, k] to
+    // alpha_k e_1 with alpha_k = -sign(a_kk) ||a[k:, k]||.
+    std::vector<double> vs(int64_t(d) * d, 0.0), diag(d);
+    int reflections = 0;
+    for (int k = 0; k < d; ++k) {
+        double nrm = 0.0;
+        for (int i = k; i < d; ++i) nrm += a[int64_t(i) * d + k] * a[int64_t(i) * d + k];
+        nrm = std::sqrt(nrm);
+        const double akk = a[int64_t(k) * d + k];
+        const double alpha = akk > 0 ? -nrm : nrm;
+        double * v = &vs[int64_t(k) * d];
+        for (int i = k; i < d; ++i) v[i] = a[int64_t(i) * d + k];
+        v[k] -= alpha;
+        double vn = 0.0;
+        for (int i = k; i < d; ++i) vn += v[i] * v[i];
+        if (k == d - 1 || vn == 0.0) {   // nothing below the diagonal: no reflection
+            for (int i = k; i < d; ++i) v[i] = 0.0;
+            diag[k] = akk;
+            continue;
+        }
+        vn = std::sqrt(vn);
+        for (int i = k; i < d; ++i) v[i] /= vn;
+        ++reflections;
+        for (int j = k; j < d; ++j) {
+            double dot = 0.0;
+            for (int i = k; i < d; ++i) dot += v[i] * a[int64_t(i) * d + j];
+            for (int i = k; i < d; ++i) a[int64_t(i) * d + j] -= 2.0 * v[i] * dot;
+        }
+        diag[k] = a[int64_t(k) * d + k];
+    }
+    // Q = H_0 H_1 ... applied to the identity from the last reflector back
+    std::vector<double> q(int64_t(d) * d, 0.0);
+    for (int i = 0; i < d; ++i) q[int64_t(i) * d + i] = 1.0;
+    for (int k = d - 1; k >= 0; --k) {
+        const double * v = &vs[int64_t(k) * d];
+        bool any = false;
+        for (int i = k; i < d; ++i) any = any || v[i] != 0.0;
+        if (!any) continue;
+        for (int j = 0; j < d; ++j) {
+            double dot = 0.0;
+            for (int i = k; i < d; ++i) dot += v[i] * q[int64_t(i) * d + j];
+            for (int i = k; i < d; ++i) q[int64_t(i) * d + j] -= 2.0 * v[i] * dot;
+        }
+    }
+    // det(H_k) = -1 for each reflection; the sign fix multiplies by the
+    // product of the diagonal's signs
+    int neg = reflections;
+    for (int j = 0; j < d; ++j) {
+        if (diag[j] < 0) {
+            ++neg;
+            for (int i = 0; i < d; ++i) q[int64_t(i) * d + j] = -q[int64_t(i) * d + j];
+        }
+    }
+    if (neg & 1)
+        for (int i = 0; i < d; ++i) q[int64_t(i) * d] = -q[int64_t(i) * d];
+    for (int64_t i = 0; i < int64_t(d) * d; ++i) r[i] = q[i];
 }
 
 int build_tables(const tq_config & cfg, int8_t * d1, int8_t * d2, float * codebook,
@@ -153,15 +278,7 @@ int build_tables(const tq_config & cfg, int8_t * d1, int8_t * d2, float * codebo
     if (cfg.qjl && s_rowmajor) {
         const uint64_t s_seed = cfg.seed ^ kSStream;
         const int64_t total = static_cast<int64_t>(m) * d;
-        for (int64_t k = 0; k < total; k += 2) {
-            uint64_t z1 = splitmix_at(s_seed, k);
-            uint64_t z2 = splitmix_at(s_seed, k + 1);
-            double u1 = std::ldexp(static_cast<double>((z1 >> 11) + 1), -53);
-            double u2 = std::ldexp(static_cast<double>(z2 >> 11), -53);
-            double r = std::sqrt(-2.0 * std::log(u1));
-            s_rowmajor[k] = static_cast<float>(r * std::cos(2.0 * M_PI * u2));
-            s_rowmajor[k + 1] = static_cast<float>(r * std::sin(2.0 * M_PI * u2));
-        }
+        for (int64_t k = 0; k < total; k += 2) box_muller(s_seed, k, s_rowmajor[k], s_rowmajor[k + 1]);
     }
     return TQ_STATUS_OK;
 }

@@ -19,7 +19,9 @@ OUT_RTOL = 5e-3
 
 def oracle_config(ctx_like):
     return oenc.Config(seed=ctx_like.seed, head_dim=ctx_like.head_dim, bits=ctx_like.bits,
-                       qjl=ctx_like.qjl)
+                       qjl=ctx_like.qjl, rotation=getattr(ctx_like, "rotation", "wht"),
+                       norm_group=getattr(ctx_like, "norm_group", 0),
+                       norm_correction=getattr(ctx_like, "norm_correction", False))
 
 
 def compare_encode(gpu, ref, cfg, tie_ok=None):
@@ -39,7 +41,17 @@ def compare_encode(gpu, ref, cfg, tie_ok=None):
            "window": int(win.sum())}
     assert rep["outside_window"] == 0, rep
     assert rep["mismatch"] <= max(MAX_WINDOW_FRACTION * diff.size, 0), rep
-    assert np.array_equal(gpu["norms"], ref["norms"]), "fp16 norms differ"
+    if cfg.norm_correction:
+        # a corrected norm depends on its group's codes: compared where they
+        # all match (a code inside the boundary window may differ)
+        L = cfg.group_len
+        grp_same = ~raw_diff.reshape(raw_diff.shape[:-1] + (cfg.head_dim // L, L)).any(axis=-1)
+        if not cfg.norm_group:
+            grp_same = grp_same[..., 0]
+        rep["norm_groups_compared"] = int(grp_same.sum())
+        assert np.array_equal(gpu["norms"][grp_same], ref["norms"][grp_same]), "fp16 norms differ"
+    else:
+        assert np.array_equal(gpu["norms"], ref["norms"]), "fp16 norms differ"
     if cfg.qjl:
         # the residual (so gamma and the signs) depends on the codes: compared
         # on the vectors whose codes all match

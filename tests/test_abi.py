@@ -79,3 +79,32 @@ def test_null_arguments_rejected_without_device():
     assert lib.tq_encode(None, None, 0, 1, 1, 1, None, binding.Planes(), None) == 1
     assert b"ctx" in lib.tq_last_error()
     assert lib.tq_attend_decode_workspace(None, None, 1, 1, 1, 1) == -1
+
+
+@pytest.mark.parametrize("seed,d", [(0, 32), (5, 64), (0, 128), (77, 256)])
+def test_haar_rotation_matches_oracle(seed, d):
+    # the library's Householder QR (C++) and the oracle's (LAPACK via numpy)
+    # are independent; with the sign and determinant fixes both give the
+    # unique rotation, equal up to float64 rounding
+    got = binding.rotation_export(seed=seed, head_dim=d, bits=3, rotation="haar")
+    want = tables.haar_rotation(seed, d)
+    assert np.abs(got - want).max() < 1e-12
+    assert np.linalg.slogdet(got)[0] == 1.0
+
+
+@pytest.mark.parametrize("seed,d", [(0, 32), (9, 128)])
+def test_wht_rotation_export_matches_oracle(seed, d):
+    got = binding.rotation_export(seed=seed, head_dim=d, bits=2)
+    assert np.abs(got - tables.rotation_matrix(seed, d)).max() < 1e-15
+
+
+def test_variant_configs_validated():
+    lib = binding.lib()
+    blk = binding.make_config(0, 128, 3, norm_group=32)
+    assert lib.tq_norm_count(ctypes.byref(blk)) == 4
+    assert lib.tq_norm_count(ctypes.byref(binding.make_config(0, 256, 3))) == 1
+    assert lib.tq_norm_count(ctypes.byref(binding.make_config(0, 128, 3, norm_group=16))) == 0
+    assert lib.tq_norm_count(ctypes.byref(binding.make_config(0, 128, 3, rotation=2))) == 0
+    # QJL keys take plain per-vector norms
+    assert lib.tq_norm_count(ctypes.byref(binding.make_config(0, 128, 3, qjl=True, norm_group=32))) == 0
+    assert lib.tq_norm_count(ctypes.byref(binding.make_config(0, 128, 3, qjl=True, norm_correction=True))) == 0

@@ -1,0 +1,164 @@
+"""GPU parity of the layout and rotation variants against the oracle:
+one fp16 norm per 32-code block, norm correction, and the dense Haar
+rotation ([TQ+ guide] §1.2, §3, §4, §5.2, §11), through the C ABI.
+
+Encode parity is element by element (codes outside the 1e-5 window, fp16
+norms bit-exact); decode and score parity run on the oracle's planes."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_quantization_05_amd import binding as tq
+from oracle import decode as odec
+from oracle import encode as oenc
+
+from _parity import LOGIT_ATOL, assert_attend_close, assert_topk_valid, compare_encode, oracle_config
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+VARIANTS = {
+    "block": dict(norm_group=32),
+    "block_corr": dict(norm_group=32, norm_correction=True),
+    "corr": dict(norm_correction=True),
+    "haar": dict(rotation="haar"),
+    "haar_corr": dict(rotation="haar", norm_correction=True),
+}
+
+
+def _say(*a):
+    print("[gpu-test]", *a, flush=True)
+
+
+def _x(shape, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(shape, generator=g) * torch.exp(0.5 * torch.randn(shape[-1], generator=g))
+    return x.to(dtype)
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_variant_encode_matches_oracle(variant, d, bits, dtype):
+    _say("variant encode", variant, d, bits, dtype)
+    ctx = tq.Context(seed=17 + d, head_dim=d, bits=bits, **VARIANTS[variant])
+    x = _x((3, 5, 67, d), dtype, seed=d * 7 + bits)    # 1005 vectors
+    x[0, 0, 0] = 0                                       # zero vector
+    x[0, 0, 1] *= 1e-3
+    x[1, 2, 3] *= 1e4
+    xg = x.reshape(15, 67, d)
+    planes = tq.encode(ctx, xg.to(DEV))
+    torch.cuda.synchronize()
+    cfg = oracle_config(ctx)
+    ref = oenc.encode(xg.float().numpy().astype(np.float64), cfg)
+    _say(compare_encode(planes.numpy(), ref, cfg))
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_variant_encode_extreme_magnitudes_and_uneven_blocks(variant, dtype):
+    # norms from ~1e-35 to ~1e35, and for block norms rotated vectors whose
+    # 32-blocks differ in scale by up to 10^6 (x = R^T y with some blocks of
+    # y scaled down).  (A block that is zero only up to rounding is no test:
+    # its codes follow the rounding noise of the rotation, in any
+    # implementation.  With one norm per vector the scaled-down blocks would
+    # put 4% of the coordinates inside the 1e-5 window around z = 0, which
+    # the N(0,1)-based cap on window mismatches does not allow for.)
+    d = 128
+    ctx = tq.Context(seed=5, head_dim=d, bits=3, **VARIANTS[variant])
+    cfg = oracle_config(ctx)
+    scales = [1e-35, 2.0 ** -61, 1.0, 2.0 ** 61, 1e35]
+    x = _x((len(scales), 40, d), torch.float32, seed=8) * torch.tensor(scales).view(-1, 1, 1)
+    R = oenc.get_tables(cfg).R
+    y = np.random.default_rng(2).standard_normal((40, d))
+    y[:, 32:64] *= 1e-6
+    y[::2, 96:] *= 1e-3
+    xz = torch.from_numpy(y @ R)
+    x = torch.cat([x.reshape(-1, d), xz.float()] if cfg.norm_group else [x.reshape(-1, d)]).to(dtype)
+    planes = tq.encode(ctx, x.to(DEV))
+    torch.cuda.synchronize()
+    ref = oenc.encode(x.float().numpy().astype(np.float64), cfg)
+    _say(variant, dtype, compare_encode(planes.numpy(), ref, cfg))
+
+
+def _oracle_planes(x, cfg):
+    out = oenc.encode(x, cfg)
+    return {k: out[k] for k in ("codes", "norms", "signs", "rnorms") if k in out}
+
+
+@pytest.mark.parametrize("kvar,vvar", [("block", "block"), ("block_corr", "corr"), ("haar", "haar"),
+                                       ("haar_corr", "haar"), ("corr", "block")])
+@pytest.mark.parametrize("d,G", [(64, 4), (128, 4), (128, 1), (256, 2)])
+def test_variant_attend_matches_oracle(kvar, vvar, d, G):
+    if VARIANTS[kvar].get("rotation") != VARIANTS[vvar].get("rotation"):
+        pytest.skip("K and V share one rotation")
+    _say("variant attend", kvar, vvar, d, G)
+    B, Hkv, T = 2, 2, 2300
+    kc = oenc.Config(seed=21, head_dim=d, bits=3, **VARIANTS[kvar])
+    vc = oenc.Config(seed=21, head_dim=d, bits=4, **VARIANTS[vvar])
+    rng = np.random.default_rng(d + G)
+    k = rng.standard_normal((B, Hkv, T, d)) * 2.0
+    v = rng.standard_normal((B, Hkv, T, d))
+    q = rng.standard_normal((B, Hkv * G, d)).astype(np.float32)
+    kp, vp = _oracle_planes(k, kc), _oracle_planes(v, vc)
+    lens = np.array([T, 1111], dtype=np.int32)
+    ref = odec.attend_decode(q.astype(np.float64), kp, vp, kc, vc, lens)
+    kctx = tq.Context(seed=21, head_dim=d, bits=3, **VARIANTS[kvar])
+    vctx = tq.Context(seed=21, head_dim=d, bits=4, **VARIANTS[vvar])
+    out = tq.attend_decode(kctx, vctx, torch.from_numpy(q).to(DEV), tq.PackedPlanes.from_numpy(kp),
+                           tq.PackedPlanes.from_numpy(vp), torch.from_numpy(lens).to(DEV))
+    torch.cuda.synchronize()
+    _say("max rel / elem / abs", assert_attend_close(out.cpu().numpy().astype(np.float64), ref))
+
+
+@pytest.mark.parametrize("variant", ["block", "block_corr", "haar", "haar_corr"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_variant_scores_match_oracle(variant, d):
+    cfg = oenc.Config(seed=4, head_dim=d, bits=4, **VARIANTS[variant])
+    rng = np.random.default_rng(d)
+    x = rng.standard_normal((1500, d)) * np.exp(0.5 * rng.standard_normal(d))
+    q = rng.standard_normal((21, d)).astype(np.float32)
+    kp = _oracle_planes(x, cfg)
+    ref = odec.scores(q.astype(np.float64), kp, cfg, scale=1 / math.sqrt(d))
+    ctx = tq.Context(seed=4, head_dim=d, bits=4, **VARIANTS[variant])
+    got = tq.scores(ctx, torch.from_numpy(q).to(DEV), tq.PackedPlanes.from_numpy(kp), top_k=0,
+                    scale=1 / math.sqrt(d))
+    s, i = tq.scores(ctx, torch.from_numpy(q).to(DEV), tq.PackedPlanes.from_numpy(kp), top_k=10,
+                     scale=1 / math.sqrt(d))
+    torch.cuda.synchronize()
+    err = float(np.abs(got.cpu().numpy() - ref).max())
+    _say(variant, d, "scores max abs err", err)
+    assert err <= LOGIT_ATOL
+    _say("top-10 agreement", assert_topk_valid(s.cpu().numpy(), i.cpu().numpy(), ref, 10))
+
+
+@pytest.mark.parametrize("d,G", [(128, 4), (256, 2)])
+def test_block_norm_attend_ignores_slots_past_each_length(d, G):
+    # slots at or past a length hold 0xFF bytes (NaN fp16 block norms); the
+    # previous launch leaves NaN-free but arbitrary LDS contents as well
+    B, Hkv, Tcap = 3, 2, 1500
+    kc = oenc.Config(seed=4, head_dim=d, bits=3, norm_group=32)
+    vc = oenc.Config(seed=4, head_dim=d, bits=4, norm_group=32, norm_correction=True)
+    rng = np.random.default_rng(5)
+    kp = _oracle_planes(rng.standard_normal((B, Hkv, Tcap, d)), kc)
+    vp = _oracle_planes(rng.standard_normal((B, Hkv, Tcap, d)), vc)
+    lens = np.array([1, 700, 1299], dtype=np.int32)
+    for planes in (kp, vp):
+        for name, arr in planes.items():
+            for b_, L in enumerate(lens):
+                arr[b_, :, L:] = np.iinfo(arr.dtype).max
+    q = rng.standard_normal((B, Hkv * G, d)).astype(np.float32)
+    ref = odec.attend_decode(q.astype(np.float64), kp, vp, kc, vc, lens)
+    kctx = tq.Context(seed=4, head_dim=d, bits=3, norm_group=32)
+    vctx = tq.Context(seed=4, head_dim=d, bits=4, norm_group=32, norm_correction=True)
+    out = tq.attend_decode(kctx, vctx, torch.from_numpy(q).to(DEV), tq.PackedPlanes.from_numpy(kp),
+                           tq.PackedPlanes.from_numpy(vp), torch.from_numpy(lens).to(DEV), t_max=Tcap)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(o))
+    _say("block norms, garbage past length", d, G, assert_attend_close(o, ref))
