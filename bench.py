@@ -29,8 +29,9 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def packed_bytes_per_token_head(w, code_bytes_k, code_bytes_v, sign_bytes_k):
-    kb = code_bytes_k + 2 + (sign_bytes_k + 2 if w.k_qjl else 0)
-    return kb + code_bytes_v + 2
+    nb = 2 * (w.d // w.norm_group if w.norm_group else 1)   # fp16 norms per vector
+    kb = code_bytes_k + nb + (sign_bytes_k + 2 if w.k_qjl else 0)
+    return kb + code_bytes_v + nb
 
 
 def traffic_from_profiles(kernel, workload):
@@ -78,8 +79,8 @@ def cpu_baseline(w, budget_s=12.0):
 
     cores, blas = _cpu_threads()
     G = w.Hq // w.Hkv
-    kc = oenc.Config(seed=w.seed, head_dim=w.d, bits=w.k_bits, qjl=w.k_qjl)
-    vc = oenc.Config(seed=w.seed, head_dim=w.d, bits=w.v_bits)
+    kc = oenc.Config(**wl.context_kwargs(w, "k"))
+    vc = oenc.Config(**wl.context_kwargs(w, "v"))
     oenc.get_tables(kc)
     oenc.get_tables(vc)
     Ts = 512
@@ -272,8 +273,8 @@ def main():
         return bench_search(args, w)
     dev = "cuda"
     torch.cuda.set_device(0)
-    kctx = tq.Context(seed=w.seed, head_dim=w.d, bits=w.k_bits, qjl=w.k_qjl)
-    vctx = tq.Context(seed=w.seed, head_dim=w.d, bits=w.v_bits)
+    kctx = tq.Context(**wl.context_kwargs(w, "k"))
+    vctx = tq.Context(**wl.context_kwargs(w, "v"))
     K, V = wl.kv_pair(w, dev)
     q = wl.queries(w, dev)
     lens = torch.full((w.B,), w.T, dtype=torch.int32, device=dev)
@@ -350,6 +351,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "Hkv": w.Hkv, "Hq": w.Hq, "head_dim": w.d,
                    "k_bits": w.k_bits, "v_bits": w.v_bits, "k_qjl": w.k_qjl, "input": w.in_dtype,
+                   "rotation": w.rotation, "norm_group": w.norm_group, "norm_correction": w.norm_correction,
                    "packed_bytes": int(packed), "rotation_copies": [R_in, R_pk]},
         "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
         "decode_us": round(dec_avg * 1e3, 2),

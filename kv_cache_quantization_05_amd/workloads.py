@@ -21,6 +21,9 @@ are not available, so these distributions stand in for real K/V):
                    values turbo4.
   llama_b4_t128k   B=4, T=131072, as llama_t32k plus 1% of the positions of
                    each batch (same for K, V and all heads) scaled x8; turbo3.
+  llama_t32k_block32  as llama_t32k with one fp16 norm per 32-code block
+                   and norm correction (3.5 bits per value at turbo3).
+  llama_t32k_haar  as llama_t32k with the dense seeded Haar rotation.
   search_1m        1,000,000 unit vectors, d=256, from a mixture of 1000
                    normalised N(0,I) centres: x = normalise(centre + 0.3 g /
                    sqrt(256)); 1024 queries drawn the same way; turbo4 + QJL
@@ -49,6 +52,9 @@ class Workload:
     outliers: int = 0          # outlier channels per head
     outlier_scale: float = 20.0
     lognormal_channels: bool = False
+    rotation: str = "wht"      # "wht" (D1.H.D2) or "haar" (dense seeded QR rotation)
+    norm_group: int = 0        # 0: one norm per vector; 32: one per 32-code block
+    norm_correction: bool = False
     seed: int = 0              # method seed (rotation, S)
     data_seed: int = 0
     extra: dict = field(default_factory=dict, compare=False, hash=False)
@@ -67,9 +73,23 @@ WORKLOADS = {
                               outliers=4),
     "llama_b4_t128k": Workload("llama_b4_t128k", 4, 131072, 8, 32, 128, 3, 3, False, "bf16",
                                outliers=4, spike_frac=0.01),
+    # layout and rotation variants of the 32K layer
+    "llama_t32k_block32": Workload("llama_t32k_block32", 1, 32768, 8, 32, 128, 3, 3, False, "bf16",
+                                   outliers=4, norm_group=32, norm_correction=True),
+    "llama_t32k_haar": Workload("llama_t32k_haar", 1, 32768, 8, 32, 128, 3, 3, False, "bf16",
+                                outliers=4, rotation="haar"),
     "search_1m": Workload("search_1m", 1, 1_000_000, 1, 1, 256, 4, 4, True, "f32",
                           extra={"centers": 1000, "sigma": 0.3, "n_queries": 1024, "top_k": 10}),
 }
+
+
+def context_kwargs(w: Workload, which="k"):
+    """Keyword arguments of a binding Context (or oracle Config) for the
+    workload's keys ("k") or values ("v")."""
+    kw = dict(seed=w.seed, head_dim=w.d, bits=w.k_bits if which == "k" else w.v_bits,
+              qjl=w.k_qjl if which == "k" else False, rotation=w.rotation, norm_group=w.norm_group,
+              norm_correction=w.norm_correction)
+    return kw
 
 
 def scaled(w: Workload, **changes) -> Workload:

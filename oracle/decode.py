@@ -129,6 +129,48 @@ def attend_decode(q, k_planes, v_planes, k_cfg: Config, v_cfg: Config, seq_lens,
     return out
 
 
+def attend_prefill(q, k_planes, v_planes, k_cfg: Config, v_cfg: Config, seq_lens, scale=None):
+    """Causal attention of a block of new positions over the packed cache.
+
+    q[B, Hq, Tq, d]: the queries of the last Tq positions of each sequence;
+    seq_lens[b] is the sequence's length including them, so query i of
+    batch b sits at position p = seq_lens[b] - Tq + i and attends the cached
+    positions j <= p (causal, [TQ explainer] §4.3 attention; the pages'
+    prefill context scaling, [TQ+ guide] §1.2, §5.3).  A query with p < 0
+    (a sequence shorter than the block) has no keys and a zero output.
+    Planes are [B, Hkv, T, ...].  Returns float64 [B, Hq, Tq, d] in the
+    original domain; keys and values are rebuilt explicitly, as in decode.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, Tq, d = q.shape
+    Hkv = k_planes["codes"].shape[1]
+    group = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.zeros((B, Hq, Tq, d))
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L <= 0:
+            continue
+        pos = L - Tq + np.arange(Tq)                    # position of each query
+        for g in range(Hkv):
+            kp = {k: v[b, g, :L] for k, v in k_planes.items()}
+            vp = {k: v[b, g, :L] for k, v in v_planes.items()}
+            K = dequant(kp, k_cfg)
+            V = dequant(vp, v_cfg, with_qjl=False)
+            visible = np.arange(L)[None, :] <= pos[:, None]          # [Tq, L] causal mask
+            for h in range(g * group, (g + 1) * group):
+                s = scale * (q[b, h] @ K.T)
+                s = np.where(visible, s, -np.inf)
+                m = s.max(axis=1, keepdims=True)
+                rows = np.isfinite(m[:, 0])
+                p = np.zeros_like(s)
+                p[rows] = np.exp(s[rows] - m[rows])
+                p[rows] /= p[rows].sum(axis=1, keepdims=True)
+                out[b, h] = p @ V
+    return out
+
+
 def top_k(score_matrix, k):
     """Indices and values of the k largest scores per row; ties -> lower index."""
     s = np.asarray(score_matrix, dtype=np.float64)

@@ -59,8 +59,8 @@ def _check_and_substitute(ctx, planes, x_head, b, g):
 def _run(name, pairs, lens_fn):
     w = wl.WORKLOADS[name]
     G = w.Hq // w.Hkv
-    kctx = tq.Context(seed=w.seed, head_dim=w.d, bits=w.k_bits, qjl=w.k_qjl)
-    vctx = tq.Context(seed=w.seed, head_dim=w.d, bits=w.v_bits)
+    kctx = tq.Context(**wl.context_kwargs(w, "k"))
+    vctx = tq.Context(**wl.context_kwargs(w, "v"))
     K, V = wl.kv_pair(w, DEV)
     q = wl.queries(w, DEV)
     kp = kctx.new_planes((w.B, w.Hkv, w.T))
@@ -110,6 +110,13 @@ def test_fullsize_llama_b16_t8k_ragged():
         return [[w.T] * w.B, [max(0, w.T - 613 * b) if b != 9 else 0 for b in range(w.B)]]
 
     _run("llama_b16_t8k", [(0, 0), (5, 3), (9, 1), (15, 7)], lens)
+
+
+@pytest.mark.parametrize("name", ["llama_t32k_block32", "llama_t32k_haar"])
+def test_fullsize_layout_and_rotation_variants(name):
+    # the 32K layer with one norm per 32-code block and norm correction, and
+    # with the dense Haar rotation, in the benchmark's launch configuration
+    _run(name, [(0, 2), (0, 6)], lambda w: [[w.T], [w.T - 3333]])
 
 
 def test_fullsize_single_head():

@@ -148,3 +148,78 @@ def test_top_k_ties_and_order():
     for r in range(7):
         ref = sorted(range(40), key=lambda j: (-s[r, j], j))[:10]
         assert idx[r].tolist() == ref
+
+
+def test_prefill_single_query_equals_decode():
+    # one new position (Tq = 1) is exactly a decode step over the cache
+    B, Hkv, Hq, T, d = 2, 2, 8, 40, 64
+    kc = Config(seed=3, head_dim=d, bits=4, qjl=True)
+    vc = Config(seed=3, head_dim=d, bits=3)
+    rng = np.random.default_rng(7)
+    kp = _planes_bhtd(rng.standard_normal((B, Hkv, T, d)), kc)
+    vp = _planes_bhtd(rng.standard_normal((B, Hkv, T, d)), vc)
+    q = rng.standard_normal((B, Hq, d))
+    lens = [T, 17]
+    pre = decode.attend_prefill(q[:, :, None, :], kp, vp, kc, vc, lens)
+    dec = decode.attend_decode(q, kp, vp, kc, vc, lens)
+    assert np.abs(pre[:, :, 0] - dec).max() < 1e-13
+
+
+def test_prefill_brute_force_tiny():
+    # explicit loops: query i of batch b at position L - Tq + i sees j <= p
+    B, Hkv, Hq, T, Tq, d = 2, 1, 2, 7, 4, 32
+    cfg = Config(seed=1, head_dim=d, bits=3)
+    rng = np.random.default_rng(3)
+    kp = _planes_bhtd(rng.standard_normal((B, Hkv, T, d)), cfg)
+    vp = _planes_bhtd(rng.standard_normal((B, Hkv, T, d)), cfg)
+    K, V = decode.dequant(kp, cfg), decode.dequant(vp, cfg)
+    q = rng.standard_normal((B, Hq, Tq, d))
+    lens = [7, 2]                                  # batch 1: positions -2, -1, 0, 1
+    got = decode.attend_prefill(q, kp, vp, cfg, cfg, lens)
+    sc = 1 / math.sqrt(d)
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(Tq):
+                p = lens[b] - Tq + i
+                if p < 0:
+                    assert np.all(got[b, h, i] == 0)
+                    continue
+                s = [sc * sum(q[b, h, i, e] * K[b, 0, j, e] for e in range(d)) for j in range(p + 1)]
+                mx = max(s)
+                w = [math.exp(x - mx) for x in s]
+                for e in range(d):
+                    want = sum(w[j] * V[b, 0, j, e] for j in range(p + 1)) / sum(w)
+                    assert abs(got[b, h, i, e] - want) < 1e-12
+
+
+def test_prefill_is_causal():
+    # changing the keys and values after a position leaves every earlier
+    # query's output unchanged, and changes the later ones
+    B, Hkv, Hq, T, d = 1, 1, 1, 30, 32
+    cfg = Config(seed=2, head_dim=d, bits=2)
+    rng = np.random.default_rng(4)
+    k = rng.standard_normal((B, Hkv, T, d))
+    v = rng.standard_normal((B, Hkv, T, d))
+    q = rng.standard_normal((B, Hq, T, d))
+    a = decode.attend_prefill(q, _planes_bhtd(k, cfg), _planes_bhtd(v, cfg), cfg, cfg, [T])
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, 20:] = rng.standard_normal((B, Hkv, 10, d))
+    v2[:, :, 20:] = rng.standard_normal((B, Hkv, 10, d))
+    b = decode.attend_prefill(q, _planes_bhtd(k2, cfg), _planes_bhtd(v2, cfg), cfg, cfg, [T])
+    assert np.array_equal(a[:, :, :20], b[:, :, :20])
+    assert np.abs(a[:, :, 20:] - b[:, :, 20:]).min(axis=-1).max() > 0
+
+
+def test_prefill_identical_keys_average_the_prefix():
+    # with every key equal, query i weighs its visible prefix uniformly
+    B, Hkv, Hq, T, d = 1, 1, 2, 12, 64
+    cfg = Config(seed=0, head_dim=d, bits=3)
+    rng = np.random.default_rng(9)
+    k = np.repeat(rng.standard_normal((1, 1, 1, d)), T, axis=2)
+    v = rng.standard_normal((B, Hkv, T, d))
+    kp, vp = _planes_bhtd(k, cfg), _planes_bhtd(v, cfg)
+    V = decode.dequant(vp, cfg)
+    out = decode.attend_prefill(rng.standard_normal((B, Hq, 5, d)), kp, vp, cfg, cfg, [T])
+    for i in range(5):
+        p = T - 5 + i
+        assert np.abs(out[0, :, i] - V[0, 0, :p + 1].mean(axis=0)).max() < 1e-12
