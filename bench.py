@@ -241,6 +241,84 @@ def cpu_baseline_search(w, bpv, budget_s=12.0):
             "encode_mtok_s": round(Ns / enc_s / 1e6, 6)}
 
 
+def bench_prefill(args, w):
+    """Prefill workload: encode the prompt's K and V into the cache (one
+    tq_encode each), then causal prefill attention of every prompt position
+    over it (tq_attend_prefill).  value = packed cache bytes per second of
+    the attention call; its roofline is the matrix-core contraction:
+    algorithmic flops 4 d per (query head, visible key) pair against the
+    dense fp16 MFMA peak."""
+    import torch
+
+    from kv_cache_quantization_05_amd import binding as tq
+    from kv_cache_quantization_05_amd import workloads as wl
+
+    dev = "cuda"
+    Tq = w.extra["Tq"]
+    kctx = tq.Context(**wl.context_kwargs(w, "k"))
+    vctx = tq.Context(**wl.context_kwargs(w, "v"))
+    K, V = wl.kv_pair(w, dev)
+    q = wl.queries(w, dev)
+    lens = torch.full((w.B,), w.T, dtype=torch.int32, device=dev)
+    kp, vp = kctx.new_planes((w.B, w.Hkv, w.T)), vctx.new_planes((w.B, w.Hkv, w.T))
+    out = torch.empty((w.B, w.Hq, Tq, w.d), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(tq.prefill_workspace_bytes(kctx, vctx, w.B, w.Hq, Tq), 1), dtype=torch.uint8, device=dev)
+    bpt = packed_bytes_per_token_head(w, kctx.code_bytes, vctx.code_bytes, kctx.sign_bytes)
+    packed = w.B * w.Hkv * w.T * bpt
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        tq.encode(kctx, K, kp)
+        tq.encode(vctx, V, vp)
+        if ev:
+            ev[1].record(stream)
+        tq.attend_prefill(kctx, vctx, q, kp, vp, lens, t_max=w.T, out=out, workspace=ws)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    enc_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs)
+    pf_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / len(evs)
+    pairs = sum(min(i + 1 + (w.T - Tq), w.T) for i in range(Tq))   # visible keys over the block
+    flops = float(w.B) * w.Hq * pairs * 4 * w.d
+    tflops = flops / (pf_ms * 1e-3) / 1e12
+    enc_bytes = (K.numel() + V.numel()) * K.element_size() + packed
+    line = {
+        "metric": "packed-KV decode-attention GB/s (% of HBM peak) + encode Mtok/s, 1 GPU",
+        "value": round(packed / (pf_ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "Tq": Tq, "Hkv": w.Hkv, "Hq": w.Hq, "head_dim": w.d,
+                   "k_bits": w.k_bits, "v_bits": w.v_bits, "k_qjl": w.k_qjl, "input": w.in_dtype,
+                   "packed_bytes": int(packed)},
+        "prefill_us": round(pf_ms * 1e3, 2),
+        "encode_us": round(enc_ms * 1e3, 2),
+        "encode_mtok_s": round(w.B * w.T / (enc_ms * 1e-3) / 1e6, 2),
+        "roofline": {"kernel": "attend_prefill", "bound": "mfma", "achieved": round(tflops, 3), "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4),
+                     "traffic": traffic_from_profiles("attend_prefill", w.name),
+                     "flops_per_launch": flops, "avg_ms": round(pf_ms, 5)},
+        "roofline_encode": {"kernel": "encode", "bound": "hbm",
+                            "achieved": round(enc_bytes / (enc_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(enc_bytes / (enc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "traffic": traffic_from_profiles("encode", w.name), "algorithmic_bytes": int(enc_bytes / 2),
+                            "avg_ms": round(enc_ms / 2, 5)},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -271,6 +349,8 @@ def main():
     w = wl.WORKLOADS[args.workload]
     if w.name == "search_1m":
         return bench_search(args, w)
+    if "Tq" in w.extra:
+        return bench_prefill(args, w)
     dev = "cuda"
     torch.cuda.set_device(0)
     kctx = tq.Context(**wl.context_kwargs(w, "k"))

@@ -226,6 +226,32 @@ int64_t tq_attend_decode_workspace(const struct tq_ctx * k_ctx, const struct tq_
                                    int32_t Hq, int32_t Hkv, int64_t t_max);
 
 /*
+ * Causal prefill attention over packed K and V ([TQ explainer] §4.3
+ * attention; [TQ+ guide] §1.2 prefill context scaling, §5.3 pre-rotated
+ * queries and the flash-attention path): the last Tq positions of each
+ * sequence attend to the cache up to and including themselves,
+ *   out[b, h, i] = sum_{j <= p} p_j v_hat_j,  p = seq_lens[b] - Tq + i,
+ *   p_j = softmax_j(scale * <q_{b,h,i}, k_hat_j>)  (QJL-corrected keys),
+ * with query head h reading KV head h / (Hq / Hkv).  A query whose position
+ * p is negative (a sequence shorter than Tq) gets a zero row.
+ * q: device fp32 [B, Hq, Tq, d] dense, 16-byte aligned.  k, v: planes over
+ * [B, Hkv, Tcap] already holding the Tq new positions (tq_encode them into
+ * the cache first).  seq_lens: device int32 [B], clamped to [0, t_max].
+ * out: device fp32 [B, Hq, Tq, d].  workspace: tq_attend_prefill_workspace()
+ * bytes.  head_dim 64, 128 or 256, one norm per vector (block-norm contexts
+ * give TQ_STATUS_UNSUPPORTED); K and V share head_dim and rotation.
+ */
+int32_t tq_attend_prefill(const struct tq_ctx * k_ctx, const struct tq_ctx * v_ctx,
+                          const float * q, struct tq_planes k, struct tq_planes v,
+                          const int32_t * seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                          int64_t Tq, int64_t t_max, float scale, float * out,
+                          void * workspace, int64_t workspace_bytes, void * hip_stream);
+
+/* Workspace bytes tq_attend_prefill needs; -1 on invalid arguments. */
+int64_t tq_attend_prefill_workspace(const struct tq_ctx * k_ctx, const struct tq_ctx * v_ctx,
+                                    int32_t B, int32_t Hq, int64_t Tq);
+
+/*
  * tq_attend_decode without a caller workspace, for callers that cannot
  * allocate device memory (code under graph capture, tight serving loops,
  * harnesses that forbid allocation).  Same arguments, semantics and results

@@ -26,7 +26,8 @@ EXPORTED = (
     "tq_ctx_create", "tq_ctx_free", "tq_tables_export", "tq_rotation_export", "tq_code_bytes",
     "tq_sign_bytes", "tq_norm_count",
     "tq_encode", "tq_scores", "tq_scores_workspace", "tq_attend_decode",
-    "tq_attend_decode_workspace", "tq_attend_decode_static", "tq_last_error", "tq_version",
+    "tq_attend_decode_workspace", "tq_attend_decode_static", "tq_attend_prefill",
+    "tq_attend_prefill_workspace", "tq_last_error", "tq_version",
 )
 
 
@@ -86,6 +87,11 @@ def lib():
         L.tq_attend_decode_static.argtypes = [vp, vp, vp, Planes, Planes, vp, i32, i32, i32, i64,
                                               ctypes.c_float, vp, vp]
         L.tq_attend_decode_static.restype = i32
+        L.tq_attend_prefill.argtypes = [vp, vp, vp, Planes, Planes, vp, i32, i32, i32, i64, i64,
+                                        ctypes.c_float, vp, vp, i64, vp]
+        L.tq_attend_prefill.restype = i32
+        L.tq_attend_prefill_workspace.argtypes = [vp, vp, i32, i32, i64]
+        L.tq_attend_prefill_workspace.restype = i64
         L.tq_attend_decode_workspace.argtypes = [vp, vp, i32, i32, i32, i64]
         L.tq_attend_decode_workspace.restype = i64
         L.tq_last_error.argtypes = []
@@ -410,6 +416,44 @@ def attend_decode_static(k_ctx: Context, v_ctx: Context, q: torch.Tensor, k: Pac
     _check(lib().tq_attend_decode_static(k_ctx.handle, v_ctx.handle, _ptr(q), k.c_struct(), v.c_struct(),
                                          _ptr(seq_lens), B, Hq, Hkv, t_max, ctypes.c_float(scale), _ptr(out),
                                          _stream_ptr(stream)))
+    return out
+
+
+def prefill_workspace_bytes(k_ctx, v_ctx, B, Hq, Tq):
+    return lib().tq_attend_prefill_workspace(k_ctx.handle, v_ctx.handle, B, Hq, Tq)
+
+
+def attend_prefill(k_ctx: Context, v_ctx: Context, q: torch.Tensor, k: PackedPlanes, v: PackedPlanes,
+                   seq_lens: torch.Tensor, t_max=None, scale=None, out=None, workspace=None, stream=None):
+    """tq_attend_prefill.  q: fp32 [B, Hq, Tq, d] (the last Tq positions of
+    each sequence); k, v: planes over [B, Hkv, Tcap] holding those positions;
+    seq_lens: int32 [B] lengths including them; returns fp32 [B, Hq, Tq, d]."""
+    _check_query(q, k_ctx, 4)
+    B, Hq, Tq, d = q.shape
+    if len(k.grid) != 3 or len(v.grid) != 3:
+        raise ValueError("k and v planes must cover a 3-D grid [B, Hkv, Tcap]")
+    Hkv = k.grid[1]
+    _check_planes(k, k_ctx, (B, Hkv), "k")
+    _check_planes(v, v_ctx, (B, Hkv), "v")
+    if not isinstance(seq_lens, torch.Tensor) or seq_lens.dtype != torch.int32 or seq_lens.numel() != B \
+            or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 tensor of B entries")
+    if t_max is None:
+        t_max = k.grid[2]
+    if t_max > k.grid[2] or t_max > v.grid[2]:
+        raise ValueError("t_max exceeds the cache capacity of the planes")
+    if scale is None:
+        scale = d ** -0.5
+    if out is not None and (out.dtype != torch.float32 or not out.is_contiguous()
+                            or tuple(out.shape) != (B, Hq, Tq, d)):
+        raise ValueError("out must be a contiguous float32 [B, Hq, Tq, d] tensor")
+    _check_on_gpu(q, seq_lens, out, *_plane_tensors(k), *_plane_tensors(v))
+    if out is None:
+        out = torch.empty((B, Hq, Tq, d), dtype=torch.float32, device=q.device)
+    workspace = _workspace(workspace, prefill_workspace_bytes(k_ctx, v_ctx, B, Hq, Tq), q.device)
+    _check(lib().tq_attend_prefill(k_ctx.handle, v_ctx.handle, _ptr(q), k.c_struct(), v.c_struct(),
+                                   _ptr(seq_lens), B, Hq, Hkv, Tq, t_max, ctypes.c_float(scale), _ptr(out),
+                                   _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
     return out
 
 

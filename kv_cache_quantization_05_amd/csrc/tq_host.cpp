@@ -365,4 +365,62 @@ int32_t tq_attend_decode(const tq_ctx * k_ctx, const tq_ctx * v_ctx, const float
     return device_status(tq::launch_attend(k_ctx->tab, v_ctx->tab, a, s), "attend launch");
 }
 
+int64_t tq_attend_prefill_workspace(const tq_ctx * k_ctx, const tq_ctx * v_ctx, int32_t B, int32_t Hq,
+                                    int64_t Tq) {
+    if (!k_ctx || !v_ctx || B < 0 || Hq < 0 || Tq < 0) return -1;
+    const int64_t rows = int64_t(B) * Hq * Tq;
+    return round_up(rows * (k_ctx->tab.d + k_ctx->tab.m) * 4) + round_up(rows * k_ctx->tab.d * 4);
+}
+
+int32_t tq_attend_prefill(const tq_ctx * k_ctx, const tq_ctx * v_ctx, const float * q, tq_planes k, tq_planes v,
+                          const int32_t * seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int64_t Tq, int64_t t_max,
+                          float scale, float * out, void * workspace, int64_t workspace_bytes, void * hip_stream) {
+    if (!k_ctx || !v_ctx) return fail(TQ_STATUS_INVALID_ARG, "k_ctx and v_ctx must be non-NULL");
+    if (k_ctx->tab.d != v_ctx->tab.d)
+        return fail(TQ_STATUS_INVALID_ARG, "k_ctx and v_ctx must share head_dim");
+    if (k_ctx->cfg.seed != v_ctx->cfg.seed || k_ctx->cfg.rotation != v_ctx->cfg.rotation)
+        return fail(TQ_STATUS_UNSUPPORTED, "k_ctx and v_ctx must share the rotation (seed and kind)");
+    if (v_ctx->cfg.qjl) return fail(TQ_STATUS_INVALID_ARG, "v_ctx must not use QJL");
+    if (k_ctx->device != v_ctx->device) return fail(TQ_STATUS_INVALID_ARG, "contexts on different devices");
+    if (B < 0 || Hq < 0 || Hkv <= 0 || Tq < 0 || t_max < 0) return fail(TQ_STATUS_INVALID_ARG, "negative sizes");
+    if (Hq % Hkv != 0) return fail(TQ_STATUS_INVALID_ARG, "Hq must be a multiple of Hkv");
+    if (B == 0 || Hq == 0 || Tq == 0) return ok();
+    const int group = Hq / Hkv;
+    if (group != 1 && group != 2 && group != 4 && group != 8)
+        return fail(TQ_STATUS_UNSUPPORTED, "Hq / Hkv must be 1, 2, 4 or 8");
+    if (!tq::prefill_supported(k_ctx->tab, v_ctx->tab))
+        return fail(TQ_STATUS_UNSUPPORTED, "prefill takes head_dim 64, 128 or 256 and one norm per vector");
+    if (!q || !out || !seq_lens) return fail(TQ_STATUS_INVALID_ARG, "q, out and seq_lens must be non-NULL");
+    if (t_max > (int64_t(1) << 31) - 1 || Tq > (int64_t(1) << 31) - 1 ||
+        int64_t(B) * Hq * Tq > (int64_t(1) << 31) - 1)
+        return fail(TQ_STATUS_UNSUPPORTED, "t_max, Tq and B * Hq * Tq are limited to 2^31 - 1");
+    if (const char * why = check_planes(k_ctx, k, k_ctx->cfg.qjl != 0))
+        return fail(TQ_STATUS_INVALID_ARG, "k: %s", why);
+    if (const char * why = check_planes(v_ctx, v, false)) return fail(TQ_STATUS_INVALID_ARG, "v: %s", why);
+    const int64_t need = tq_attend_prefill_workspace(k_ctx, v_ctx, B, Hq, Tq);
+    if (!workspace || workspace_bytes < need)
+        return fail(TQ_STATUS_INVALID_ARG, "workspace too small: need %lld bytes", (long long)need);
+    if (!aligned(workspace, 256)) return fail(TQ_STATUS_INVALID_ARG, "workspace must be 256-byte aligned");
+    if (!aligned(q, 16)) return fail(TQ_STATUS_INVALID_ARG, "q must be 16-byte aligned");
+    const int64_t rows = int64_t(B) * Hq * Tq;
+    char * ws = static_cast<char *>(workspace);
+    tq::prefill_args a{};
+    a.q = q;
+    a.qp = reinterpret_cast<float *>(ws);
+    a.qp_stride = k_ctx->tab.d + k_ctx->tab.m;
+    a.k = k;
+    a.v = v;
+    a.seq_lens = seq_lens;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Tq = Tq;
+    a.t_max = t_max;
+    a.scale = scale;
+    a.out_rot = reinterpret_cast<float *>(ws + round_up(rows * a.qp_stride * 4));
+    a.out = out;
+    return device_status(tq::launch_prefill(k_ctx->tab, v_ctx->tab, a, static_cast<hipStream_t>(hip_stream)),
+                         "prefill launch");
+}
+
 }  // extern "C"

@@ -97,6 +97,22 @@ int current_cu_count();
 int attend_chunk_tokens(const dev_tables & kt, const dev_tables & vt, int32_t B, int32_t Hq, int32_t Hkv,
                         int64_t t_max);
 
+struct prefill_args {
+    const float * q;            // queries [B*Hq*Tq, d] as given
+    float * qp;                 // prepared queries [B*Hq*Tq, qp_stride] (workspace)
+    int64_t qp_stride;
+    tq_planes k, v;
+    const int32_t * seq_lens;   // lengths including the Tq new positions
+    int32_t B, Hq, Hkv;
+    int64_t Tq;
+    int64_t t_max;
+    float scale;
+    float * out_rot;            // rotated-domain outputs [B*Hq*Tq, d] (workspace)
+    float * out;                // [B*Hq*Tq, d]
+};
+bool prefill_supported(const dev_tables & kt, const dev_tables & vt);
+hipError_t launch_prefill(const dev_tables & kt, const dev_tables & vt, const prefill_args & a, hipStream_t s);
+
 struct scores_args {
     const float * qp;
     int64_t qp_stride;

@@ -14,7 +14,9 @@ units of a plain copy of known size.  Databases are deleted after reading
 
 Launch groups: one tq_attend_decode call runs the split-K kernel, the merge
 kernel and (for QJL keys or the generic path) the query kernel, so its
-figures are sums over those kernels per merge dispatch; one tq_encode call
+figures are sums over those kernels per merge dispatch; one
+tq_attend_prefill call runs the query kernel, the prefill kernel and the
+rotation back, counted per prefill dispatch; one tq_encode call
 runs one encode kernel, so its figures are averages over encode dispatches
 (K and V launches alike); one tq_scores call runs the query kernel, the
 scorer and (top-k) the list merge, counted per scorer dispatch.  The query
@@ -34,15 +36,19 @@ GIB = 1 << 30
 
 GROUPS = {
     "attend_decode": re.compile(r"attend_mfma_kernel|attend_partial_kernel|attend_merge_kernel|query_prep_kernel"),
-    "encode": re.compile(r"encode_kernel|encode_qjl_kernel|encode_mfma_kernel"),
+    "attend_prefill": re.compile(r"prefill_kernel|rotate_back_kernel"),
+    "encode": re.compile(r"encode_kernel|encode_qjl_kernel|encode_mfma_kernel|encode_var_kernel|encode_haar_kernel"),
     "scores": re.compile(r"scores_mfma_kernel|scores_topk_kernel|scores_full_kernel|topk_merge_kernel"),
 }
 # dispatches that count launches of each group
 ANCHORS = {"attend_decode": re.compile(r"attend_merge_kernel"), "encode": GROUPS["encode"],
+           "attend_prefill": re.compile(r"prefill_kernel"),
            "scores": re.compile(r"scores_mfma_kernel|scores_topk_kernel|scores_full_kernel")}
 QUERY = re.compile(r"query_prep_kernel")
 DECODE_ONLY = re.compile(r"attend_mfma_kernel|attend_partial_kernel|attend_merge_kernel")
+PREFILL = re.compile(r"prefill_kernel")
 _has_decode = [True]
+_has_prefill = [False]
 
 
 def kernel_source_hash():
@@ -95,8 +101,9 @@ def read_counter(d, counter):
 
 
 def group_of(name):
+    # the query kernel belongs to the call that ran it: decode, prefill or scores
     if QUERY.search(name) and not _has_decode[0]:
-        return "scores"
+        return "attend_prefill" if _has_prefill[0] else "scores"
     for g, rx in GROUPS.items():
         if rx.search(name):
             return g
@@ -120,6 +127,7 @@ def main():
         out.append(f"# commands: {args.command}")
     trace = read_trace(args.trace)
     _has_decode[0] = any(DECODE_ONLY.search(r[0]) for r in trace)
+    _has_prefill[0] = any(PREFILL.search(r[0]) for r in trace)
     out.append("## kernel trace (durations in us)")
     out.append("kernel | calls | avg_us | min_us | max_us | vgpr | lds | scratch | blocks")
     per_group = {}

@@ -24,6 +24,10 @@ are not available, so these distributions stand in for real K/V):
   llama_t32k_block32  as llama_t32k with one fp16 norm per 32-code block
                    and norm correction (3.5 bits per value at turbo3).
   llama_t32k_haar  as llama_t32k with the dense seeded Haar rotation.
+  llama_prefill_t8k  an 8K prompt of the 32K layer's shape and distribution:
+                   its K and V encoded into the cache, then causal prefill
+                   attention of all 8192 positions (fp32 N(0,1) queries
+                   [B, Hq, Tq, d]).
   search_1m        1,000,000 unit vectors, d=256, from a mixture of 1000
                    normalised N(0,I) centres: x = normalise(centre + 0.3 g /
                    sqrt(256)); 1024 queries drawn the same way; turbo4 + QJL
@@ -78,6 +82,9 @@ WORKLOADS = {
                                    outliers=4, norm_group=32, norm_correction=True),
     "llama_t32k_haar": Workload("llama_t32k_haar", 1, 32768, 8, 32, 128, 3, 3, False, "bf16",
                                 outliers=4, rotation="haar"),
+    # prefill: a whole 8K prompt encoded into the cache and attended causally
+    "llama_prefill_t8k": Workload("llama_prefill_t8k", 1, 8192, 8, 32, 128, 3, 3, False, "bf16",
+                                  outliers=4, extra={"Tq": 8192}),
     "search_1m": Workload("search_1m", 1, 1_000_000, 1, 1, 256, 4, 4, True, "f32",
                           extra={"centers": 1000, "sigma": 0.3, "n_queries": 1024, "top_k": 10}),
 }
@@ -154,9 +161,11 @@ def kv_pair(w: Workload, device="cpu", batches=None):
 
 
 def queries(w: Workload, device="cpu"):
-    """fp32 N(0,1) decode queries [B, Hq, d]."""
+    """fp32 N(0,1) decode queries [B, Hq, d], or [B, Hq, Tq, d] for a prefill
+    workload."""
     g = _gen(device, 2000 + w.data_seed)
-    return torch.randn((w.B, w.Hq, w.d), generator=g, device=device, dtype=torch.float32)
+    shape = (w.B, w.Hq, w.extra["Tq"], w.d) if "Tq" in w.extra else (w.B, w.Hq, w.d)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
 
 
 def search_set(w: Workload, device="cpu", n=None, n_queries=None):
