@@ -17,9 +17,9 @@
 // 8 consecutive tokens the lane supplies at k-slots 8 (l / 16) .. + 7 of
 // the value product.  No data moves between the two products.
 //
-// A workgroup owns one (batch, KV head) and 64 NCT query rows (P positions
-// x G heads); per 64-token tile its 256 threads dequantise the keys (row
-// major) and values (transposed) into LDS once for all four waves.  Online
+// A workgroup owns one (batch, KV head) and 16 NCT NW query rows (P
+// positions x G heads); per 64-token tile its threads dequantise the keys
+// (row major) and values (transposed) into LDS once for all NW waves.  Online
 // softmax in base-2 units per query column; value norms enter the weights,
 // scaled per tile by the tile's largest norm so they stay in [0, 1] in fp16.
 // The output stays in the rotated domain; a second kernel rotates it back.
@@ -49,21 +49,21 @@ __device__ __forceinline__ int tile_token(int rt, int r) {
     return 32 * (rt >> 1) + 8 * (r >> 2) + 4 * (rt & 1) + (r & 3);
 }
 
-template <int D, int KB, int VB, bool QJL, int NCT>
-__global__ __launch_bounds__(256) void prefill_kernel(const dev_tables kt, const dev_tables vt, const prefill_args a) {
+template <int D, int KB, int VB, bool QJL, int NCT, int NW>
+__global__ __launch_bounds__(64 * NW) void prefill_kernel(const dev_tables kt, const dev_tables vt, const prefill_args a) {
     constexpr int KS = D / 32;          // k-steps of the logits
     constexpr int DT = D / 16;          // 16-dim tiles of the output
     constexpr int KRS = D + 8;          // key rows in LDS (halves): rows 16 B apart in the banks
     constexpr int VRS = kPT + 8;        // value rows (one per dim) in LDS
     __shared__ __align__(16) uint16_t klds[kPT * KRS];
     __shared__ __align__(16) uint16_t vlds[D * VRS];
-    __shared__ float knl[kPT], vnl[kPT], krl[QJL ? kPT : 1];
+    __shared__ __align__(16) float knl[kPT], vnl[kPT], krl[QJL ? kPT : 1];
     __shared__ uint32_t ksl[QJL ? kPT : 1][QJL ? D / 32 : 1];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int c16 = lane & 15, g4 = lane >> 4;
     const int G = a.Hq / a.Hkv;
-    const int rows = 64 * NCT;                     // query rows of the workgroup
+    const int rows = 16 * NW * NCT;                // query rows of the workgroup
     const int P = rows / G;                        // positions of the workgroup
     const int qt = gridDim.x - 1 - blockIdx.x;     // latest positions (most keys) first
     const int g = blockIdx.y, b = blockIdx.z;
@@ -118,6 +118,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const dev_tables kt, const
 
     f32x4 acc[NCT][DT];
     float m_run[NCT], l_run[NCT];
+    float vrun = 0.f;   // running largest value weight scale: acc is in units of it
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
         m_run[ct] = -INFINITY;
@@ -130,54 +131,83 @@ __global__ __launch_bounds__(256) void prefill_kernel(const dev_tables kt, const
 
     for (int64_t t0 = 0; t0 < kend; t0 += kPT) {
         __syncthreads();   // the previous tile's LDS reads are done
-        // ---- dequantise the tile: unit (token, 32-code block)
-        for (int u = tid; u < kPT * KS; u += 256) {
-            const int tt = u / KS, bl = u % KS;
+        // ---- dequantise the tile: unit (token, 32-code block), a wave's 64
+        // lanes taking one block of the tile's 64 tokens, so the transposed
+        // value stores of one instruction fill consecutive halves of one row
+        // (with 8 waves, waves 0-3 decode the keys and waves 4-7 the values)
+        const bool do_k = NW == 4 || tid < 256, do_v = NW == 4 || tid >= 256;
+        for (int u = tid & 255; u < kPT * KS; u += 256) {
+            const int tt = u % kPT, bl = u / kPT;
             const int64_t t = t0 + tt;
             const bool ok = t < kend;
-            uint32_t kw[KB], vw[VB];
-            const int64_t kv = kvb + t * a.k.stride[2], vv = vvb + t * a.v.stride[2];
-            const uint32_t * kc = reinterpret_cast<const uint32_t *>(a.k.codes + kv * (D * KB / 8)) + bl * KB;
-            const uint32_t * vc = reinterpret_cast<const uint32_t *>(a.v.codes + vv * (D * VB / 8)) + bl * VB;
+            if (do_k) {
+                const int64_t kv = kvb + t * a.k.stride[2];
+                const uint32_t * kc = reinterpret_cast<const uint32_t *>(a.k.codes + kv * (D * KB / 8)) + bl * KB;
+                uint32_t kw[KB];
 #pragma unroll
-            for (int k = 0; k < KB; ++k) kw[k] = ok ? kc[k] : 0u;
+                for (int k = 0; k < KB; ++k) kw[k] = ok ? kc[k] : 0u;
+                uint32_t kp[16];
 #pragma unroll
-            for (int k = 0; k < VB; ++k) vw[k] = ok ? vc[k] : 0u;
-            uint32_t kp[16];
+                for (int q4 = 0; q4 < 8; ++q4) {
+                    uint32_t sel = 0;
 #pragma unroll
-            for (int q4 = 0; q4 < 8; ++q4) {
-                uint32_t sel = 0, vsel = 0;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    sel |= block_code<KB>(kw, 4 * q4 + j) << (8 * j);
-                    vsel |= block_code<VB>(vw, 4 * q4 + j) << (8 * j);
+                    for (int j = 0; j < 4; ++j) sel |= block_code<KB>(kw, 4 * q4 + j) << (8 * j);
+                    lut4<KB>(klut, sel, kp[2 * q4], kp[2 * q4 + 1]);
                 }
-                lut4<KB>(klut, sel, kp[2 * q4], kp[2 * q4 + 1]);
-                uint32_t v0, v1;
-                lut4<VB>(vlut, vsel, v0, v1);
-                const int dim0 = 32 * bl + 4 * q4;
-                vlds[(dim0 + 0) * VRS + tt] = static_cast<uint16_t>(v0);
-                vlds[(dim0 + 1) * VRS + tt] = static_cast<uint16_t>(v0 >> 16);
-                vlds[(dim0 + 2) * VRS + tt] = static_cast<uint16_t>(v1);
-                vlds[(dim0 + 3) * VRS + tt] = static_cast<uint16_t>(v1 >> 16);
-            }
-            uint4 * kd = reinterpret_cast<uint4 *>(&klds[tt * KRS + 32 * bl]);
+                uint4 * kd = reinterpret_cast<uint4 *>(&klds[tt * KRS + 32 * bl]);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) kd[c] = uint4{kp[4 * c], kp[4 * c + 1], kp[4 * c + 2], kp[4 * c + 3]};
-            if constexpr (QJL) ksl[tt][bl] = ok ? reinterpret_cast<const uint32_t *>(a.k.signs + kv * (D / 8))[bl] : 0u;
-            if (bl == 0) {
-                knl[tt] = ok ? half_bits_to_float(a.k.norms[kv]) : 0.f;
-                vnl[tt] = ok ? half_bits_to_float(a.v.norms[vv]) * inv_sqrt_d : 0.f;
-                if constexpr (QJL) krl[tt] = ok ? half_bits_to_float(a.k.rnorms[kv]) * qjl_coef : 0.f;
+                for (int c = 0; c < 4; ++c) kd[c] = uint4{kp[4 * c], kp[4 * c + 1], kp[4 * c + 2], kp[4 * c + 3]};
+                if constexpr (QJL) ksl[tt][bl] = ok ? reinterpret_cast<const uint32_t *>(a.k.signs + kv * (D / 8))[bl] : 0u;
+                if (bl == 0) {
+                    // per-token factors: the key norm with the logit scale (base
+                    // 2) and 1/sqrt(d); the QJL term's gamma sqrt(pi/2)/m on top
+                    const float nk = ok ? half_bits_to_float(a.k.norms[kv]) * s2scale : 0.f;
+                    knl[tt] = nk * inv_sqrt_d;
+                    if constexpr (QJL) krl[tt] = ok ? half_bits_to_float(a.k.rnorms[kv]) * qjl_coef * nk : 0.f;
+                }
+            }
+            if (do_v) {
+                const int64_t vv = vvb + t * a.v.stride[2];
+                const uint32_t * vc = reinterpret_cast<const uint32_t *>(a.v.codes + vv * (D * VB / 8)) + bl * VB;
+                uint32_t vw[VB];
+#pragma unroll
+                for (int k = 0; k < VB; ++k) vw[k] = ok ? vc[k] : 0u;
+#pragma unroll
+                for (int q4 = 0; q4 < 8; ++q4) {
+                    uint32_t vsel = 0;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) vsel |= block_code<VB>(vw, 4 * q4 + j) << (8 * j);
+                    uint32_t v0, v1;
+                    lut4<VB>(vlut, vsel, v0, v1);
+                    const int dim0 = 32 * bl + 4 * q4;
+                    vlds[(dim0 + 0) * VRS + tt] = static_cast<uint16_t>(v0);
+                    vlds[(dim0 + 1) * VRS + tt] = static_cast<uint16_t>(v0 >> 16);
+                    vlds[(dim0 + 2) * VRS + tt] = static_cast<uint16_t>(v1);
+                    vlds[(dim0 + 3) * VRS + tt] = static_cast<uint16_t>(v1 >> 16);
+                }
+                if (bl == 0) vnl[tt] = ok ? half_bits_to_float(a.v.norms[vv]) * inv_sqrt_d : 0.f;
             }
         }
         __syncthreads();
-        // the tile's largest value weight scale (weights stay in [0, 1] in fp16)
-        float vmax = fmaxf(vnl[lane], 0.f);
+        // the running largest value weight scale (weights stay in [0, 1] in
+        // fp16); the same in every wave of the workgroup
+        float vmax = vnl[lane];
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, o));
-        const float vscale = vmax > 0.f ? vmax : 1.f;
-        const float inv_vscale = 1.0f / vscale;
+        const float vnew = fmaxf(vrun, vmax);
+        const float vrescale = vnew > vrun && vrun > 0.f ? vrun / vnew : 1.f;   // acc to the new units
+        vrun = vnew;
+        const float inv_v = vrun > 0.f ? 1.0f / vrun : 0.f;
+        // per-token factors of this lane's 16 tokens (4 consecutive per key tile)
+        float4 kf[4], vf[4], kq[QJL ? 4 : 1];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const int t4 = 32 * (rt >> 1) + 8 * g4 + 4 * (rt & 1);
+            kf[rt] = *reinterpret_cast<const float4 *>(&knl[t4]);
+            vf[rt] = *reinterpret_cast<const float4 *>(&vnl[t4]);
+            if constexpr (QJL) kq[rt] = *reinterpret_cast<const float4 *>(&krl[t4]);
+        }
+        const bool tile_full = t0 + kPT <= kend;
 
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
@@ -203,20 +233,23 @@ __global__ __launch_bounds__(256) void prefill_kernel(const dev_tables kt, const
                     }
                 }
             }
-            // ---- scale, mask, running maximum (base 2)
+            // ---- scale, mask, running maximum (base 2); tiles wholly below
+            // every column's position need no mask
             float x[4][4];
             float mt = -INFINITY;
+            const bool nomask = __all(qvalid[ct] && tile_full && t0 + kPT - 1 <= qpos[ct]);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int tt = 32 * (rt >> 1) + 8 * g4 + 4 * (rt & 1) + j;
-                    float v = s[rt][j] * inv_sqrt_d;
-                    if constexpr (QJL) v = fmaf(krl[tt], su[rt][j], v);
-                    v *= knl[tt] * s2scale;
-                    const int64_t t = t0 + tt;
-                    x[rt][j] = (qvalid[ct] && t <= qpos[ct] && t < kend) ? v : -INFINITY;
-                    mt = fmaxf(mt, x[rt][j]);
+                    float v = s[rt][j] * kf[rt][j];
+                    if constexpr (QJL) v = fmaf(kq[rt][j], su[rt][j], v);
+                    if (!nomask) {
+                        const int64_t t = t0 + 32 * (rt >> 1) + 8 * g4 + 4 * (rt & 1) + j;
+                        v = (qvalid[ct] && t <= qpos[ct] && t < kend) ? v : -INFINITY;
+                    }
+                    x[rt][j] = v;
+                    mt = fmaxf(mt, v);
                 }
             mt = fmaxf(mt, __shfl_xor(mt, 16));
             mt = fmaxf(mt, __shfl_xor(mt, 32));
@@ -232,25 +265,28 @@ __global__ __launch_bounds__(256) void prefill_kernel(const dev_tables kt, const
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int tt = 32 * (rt >> 1) + 8 * g4 + 4 * (rt & 1) + j;
-                    const float p = exp2f(x[rt][j] - m_use);
+                    const float p = __builtin_amdgcn_exp2f(x[rt][j] - m_use);
                     ps += p;
-                    w[rt >> 1][4 * (rt & 1) + j] = static_cast<_Float16>(p * (vnl[tt] * inv_vscale));
+                    w[rt >> 1][4 * (rt & 1) + j] = static_cast<_Float16>(p * (vf[rt][j] * inv_v));
                 }
             ps += __shfl_xor(ps, 16);
             ps += __shfl_xor(ps, 32);
             l_run[ct] = l_run[ct] * corr + ps;
-            // ---- O^T += V^T W (value norms folded into the weights, /vscale)
-            const float pre = corr * inv_vscale;
+            // ---- O^T += V^T W (value norms folded into the weights, in units
+            // of the running scale); the rescale is skipped when no column of
+            // the wave needs one (the common case once the maxima settle)
+            const float pre = corr * vrescale;
+            if (!__all(pre == 1.f)) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc[ct][dt] *= pre;
+            }
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                acc[ct][dt] *= pre;
 #pragma unroll
                 for (int k2 = 0; k2 < 2; ++k2) {
                     const f16x8 av = lds_f16x8(&vlds[(16 * dt + c16) * VRS + 32 * k2 + 8 * g4]);
                     acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, w[k2], acc[ct][dt], 0, 0, 0);
                 }
-                acc[ct][dt] *= vscale;
             }
         }
     }
@@ -258,7 +294,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const dev_tables kt, const
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
         if (!qvalid[ct]) continue;
-        const float inv = l_run[ct] > 0.f ? 1.0f / l_run[ct] : 0.f;
+        const float inv = l_run[ct] > 0.f ? vrun / l_run[ct] : 0.f;
         float * dst = a.out_rot + qrow[ct] * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
@@ -302,12 +338,16 @@ __global__ __launch_bounds__(256) void rotate_back_kernel(const dev_tables t, co
 
 template <int D, int KB, int VB, bool QJL>
 hipError_t launch_t(const dev_tables & kt, const dev_tables & vt, const prefill_args & a, hipStream_t s) {
+    // four waves per workgroup (eight sharing each dequantised tile measured
+    // 16% slower at 8K); one column tile per wave at d = 256, where the query
+    // operands and accumulators of two would fill the registers
     constexpr int NCT = D >= 256 ? 1 : 2;
+    constexpr int NW = 4;
     const int G = a.Hq / a.Hkv;
-    const int P = 64 * NCT / G;
+    const int P = 16 * NW * NCT / G;
     const int64_t tiles = (a.Tq + P - 1) / P;
     const dim3 grid(static_cast<uint32_t>(tiles), a.Hkv, a.B);
-    hipLaunchKernelGGL((prefill_kernel<D, KB, VB, QJL, NCT>), grid, dim3(256), 0, s, kt, vt, a);
+    hipLaunchKernelGGL((prefill_kernel<D, KB, VB, QJL, NCT, NW>), grid, dim3(64 * NW), 0, s, kt, vt, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((rotate_back_kernel<D>), dim3(static_cast<uint32_t>(int64_t(a.B) * a.Hq * a.Tq)), dim3(D), 0, s,
