@@ -64,6 +64,14 @@ static_assert(kG * (kD + 2) * 4 <= kWaveLds, "wave results fit the wave's LDS");
 constexpr float kSlack = 10.0f;  // w <= e^10 ~ 2.2e4 stays well inside fp16
 constexpr int kRsrcWord3 = 0x00020000;
 
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// Largest of four fp16 norms packed in two dwords.
+__device__ __forceinline__ float max_norm4(u32x2 w) {
+    return fmaxf(fmaxf(half_bits_to_float(static_cast<uint16_t>(w.x & 0xFFFFu)), half_bits_to_float(static_cast<uint16_t>(w.x >> 16))),
+                 fmaxf(half_bits_to_float(static_cast<uint16_t>(w.y & 0xFFFFu)), half_bits_to_float(static_cast<uint16_t>(w.y >> 16))));
+}
+
 __device__ __forceinline__ half4 tr_read4(const uint8_t * lds_base, int off) {
     const shortx4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(lds_base + off));
     half4 h;
@@ -152,13 +160,17 @@ __device__ __forceinline__ void buf_dwords(__amdgpu_buffer_rsrc_t r, uint32_t vo
     }
 }
 
-template <int KB, int VB, bool QJL>
+template <int KB, int VB, bool QJL, bool BN>
 struct step_regs {
     uint32_t kw[4 * KB];     // K code block lane/16 of tokens lane%16 + 16 tg, tg = 0..3
     uint32_t vw[kPasses][VB];  // V block (lane>>4) of token 16 pass + (lane&15)
     uint32_t ks[QJL ? 4 : 1];
     uint16_t kr;             // QJL residual norm
     uint16_t nk, nv;         // K and V norms of token lane
+    // block norms: K norm of block lane/16 of token lane%16 + 16 tg; the four
+    // V norms of each pass's token and (last) of token lane
+    uint16_t nkb[BN ? 4 : 1];
+    u32x2 nvb[BN ? kPasses + 1 : 1];
 };
 
 // Waves per SIMD the register budget is sized for: 2 (at most 256 VGPRs; two
@@ -179,10 +191,19 @@ constexpr int waves_per_simd() {
     return (!QJL && VB == 3 && KB <= 3) ? 2 : 1;
 }
 
-template <int KB, int VB, bool QJL>
+template <int KB, int VB, bool QJL, bool BN>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, 256), amdgpu_waves_per_eu(waves_per_simd<KB, VB, QJL>())))
 void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
                                                           const attend_args a) {
+    // BN: one norm per 32-code block for keys and values.  The logits then
+    // use rows 4 blk + h of the 16x16x32 product (head h restricted to block
+    // blk, hi and lo parts in two products), so each lane gets the four
+    // heads' partial logits of its block, weights them by that block's norm,
+    // and the row swaps that place token group tg in lane group tg also sum
+    // the four blocks.  A value block is scaled by its norm over the token's
+    // largest block norm (<= 1, exact enough in fp16), and the token's
+    // softmax weight carries that largest norm.
+    constexpr int NN = BN ? 4 : 1;  // norms per vector
     constexpr uint32_t kKcb = kD * KB / 8, kVcb = kD * VB / 8;
     // one LDS array: the 3/4-bit byte tables (keys in the low half of each
     // 256-byte entry, values in the high half) at offset 0, where a byte
@@ -221,9 +242,9 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     const int64_t kvec = int64_t(b) * a.k.stride[0] + int64_t(g) * a.k.stride[1];
     const int64_t vvec = int64_t(b) * a.v.stride[0] + int64_t(g) * a.v.stride[1];
     const uint8_t * const kc0 = a.k.codes + kvec * kKcb;
-    const uint16_t * const kn0 = a.k.norms + kvec;
+    const uint16_t * const kn0 = a.k.norms + kvec * NN;
     const uint8_t * const vc0 = a.v.codes + vvec * kVcb;
-    const uint16_t * const vn0 = a.v.norms + vvec;
+    const uint16_t * const vn0 = a.v.norms + vvec * NN;
     const uint8_t * const ks0 = QJL ? a.k.signs + kvec * (kD / 8) : nullptr;
     const uint16_t * const kr0 = QJL ? a.k.rnorms + kvec : nullptr;
     // per-lane byte offsets relative to the step's first token
@@ -237,8 +258,17 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
 #pragma unroll
     for (int hp = 0; hp < kPasses; ++hp)
         vo_v[hp] = uint32_t(kPass * hp + 4 * (lane >> 4) + (lane & 3)) * vs2 * kVcb + ((lane >> 2) & 3) * 4 * VB;
+    // block norms: K block lane/16 of token lane%16 + 16 tg; V norms of the
+    // pass tokens (as above) and of token lane
+    uint32_t vo_knb[BN ? 4 : 1], vo_vnb[BN ? kPasses : 1];
+    if constexpr (BN) {
+#pragma unroll
+        for (int tg = 0; tg < 4; ++tg) vo_knb[tg] = (uint32_t((lane & 15) + 16 * tg) * ks2 * 4 + (lane >> 4)) * 2;
+#pragma unroll
+        for (int hp = 0; hp < kPasses; ++hp) vo_vnb[hp] = uint32_t(kPass * hp + 4 * (lane >> 4) + (lane & 3)) * vs2 * 8;
+    }
 
-    using regs = step_regs<KB, VB, QJL>;
+    using regs = step_regs<KB, VB, QJL, BN>;
     auto load_step = [&](int64_t j0, regs & r) {
         const int64_t j = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(j0 < w_end ? j0 : L));  // wave-uniform
         const uint32_t left = static_cast<uint32_t>(L - j);  // tokens from j to L (0 past the end)
@@ -249,8 +279,18 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc0 + vj * kVcb, left * vs2 * kVcb);
 #pragma unroll
         for (int hp = 0; hp < kPasses; ++hp) buf_dwords<VB>(rv, vo_v[hp], 0, r.vw[hp]);
-        r.nk = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(kn0 + kj, left * ks2 * 2), vo_kn, 0, 0);
-        r.nv = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(vn0 + vj, left * vs2 * 2), vo_vn, 0, 0);
+        if constexpr (BN) {
+            const __amdgpu_buffer_rsrc_t rkn = make_rsrc(kn0 + kj * 4, left * ks2 * 8);
+#pragma unroll
+            for (int tg = 0; tg < 4; ++tg) r.nkb[tg] = __builtin_amdgcn_raw_buffer_load_b16(rkn, vo_knb[tg], 0, 0);
+            const __amdgpu_buffer_rsrc_t rvn = make_rsrc(vn0 + vj * 4, left * vs2 * 8);
+#pragma unroll
+            for (int hp = 0; hp < kPasses; ++hp) r.nvb[hp] = __builtin_amdgcn_raw_buffer_load_b64(rvn, vo_vnb[hp], 0, 0);
+            r.nvb[kPasses] = __builtin_amdgcn_raw_buffer_load_b64(rvn, vo_vn * 4, 0, 0);
+        } else {
+            r.nk = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(kn0 + kj, left * ks2 * 2), vo_kn, 0, 0);
+            r.nv = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(vn0 + vj, left * vs2 * 2), vo_vn, 0, 0);
+        }
         if constexpr (QJL) {
             buf_dwords<4>(make_rsrc(ks0 + kj * (kD / 8), left * ks2 * (kD / 8)), vo_ks, 0, r.ks);
             r.kr = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(kr0 + kj, left * ks2 * 2), vo_kn, 0, 0);
@@ -391,8 +431,24 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     // the 4 k-steps ks, i.e. dims 32 (l / 16) + pos(8 ks + e) of code block
     // l / 16; rows 0..3 are the fp16 hi parts of heads 0..3, rows 4..7 the lo
     // parts, rows 8..15 zero.
-    half8 aqk[4];
-    {
+    half8 aqk[4], aql[BN ? 4 : 1];
+    if constexpr (BN) {
+        // rows 4 blk + h: head h on block blk's k-slots (lane group blk), zero
+        // elsewhere; hi parts in aqk, lo parts in aql
+        const int row = lane & 15, bl = lane >> 4;
+        const float * qrow = qsrc + (row & 3) * qstride;
+        const bool mine = (row >> 2) == bl;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = qrow[32 * bl + decoded_code_of_pos<KB>(8 * ks + e)];
+                const _Float16 hi = static_cast<_Float16>(x);
+                const _Float16 lo = static_cast<_Float16>(x - static_cast<float>(hi));
+                aqk[ks][e] = mine ? hi : static_cast<_Float16>(0.f);
+                aql[ks][e] = mine ? lo : static_cast<_Float16>(0.f);
+            }
+    } else {
         const int row = lane & 15, bl = lane >> 4;
         const float * qrow = qsrc + (row & 3) * qstride;
 #pragma unroll
@@ -426,7 +482,7 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     const float inv_sqrt_d = 1.0f / sqrtf(float(kD));
     // logits are kept in base-2 units (scaled by log2 e), so weights are plain
     // exp2; the reference is converted back to natural units at the end
-    const float kscale = a.scale * inv_sqrt_d * float(M_LOG2E);
+    const float kscale = a.scale * (BN ? 1.0f / sqrtf(32.f) : inv_sqrt_d) * float(M_LOG2E);
     const float qjl_gain = sqrtf(0.5f * float(M_PI)) / float(kD) * sqrtf(float(kD));
     const float w_cap = __expf(kSlack);
 
@@ -476,11 +532,31 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
                 unpack_block<KB>(klut, wb, bq);
             }
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
+            for (int ks = 0; ks < 4; ++ks) {
                 D[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aqk[ks], as_half8(bq + 4 * ks), D[tg], 0, 0, 0);
+                if constexpr (BN)
+                    D[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aql[ks], as_half8(bq + 4 * ks), D[tg], 0, 0, 0);
+            }
+            if constexpr (BN) {
+                const float nb = half_bits_to_float(r.nkb[tg]);   // norm of block lane/16
+#pragma unroll
+                for (int h = 0; h < kG; ++h) D[tg][h] *= nb;
+            }
         }
         floatx4 S;
-        {
+        if constexpr (BN) {
+            // rows of D[tg]: lane group = block; sum the four blocks while
+            // moving token group tg to lane group tg
+#pragma unroll
+            for (int h = 0; h < kG; ++h) {
+                const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(D[0][h]), __float_as_uint(D[1][h]), false, false);
+                const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(D[2][h]), __float_as_uint(D[3][h]), false, false);
+                const float a01 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+                const float a23 = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+                const auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(a01), __float_as_uint(a23), false, false);
+                S[h] = __uint_as_float(z[0]) + __uint_as_float(z[1]);
+            }
+        } else {
             floatx4 P0, P1;
 #pragma unroll
             for (int h = 0; h < kG; ++h) {
@@ -513,8 +589,14 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
         }
         // ---------------- online softmax over the wave's tokens
         const bool own = j0 + lane < w_end;
-        const float ks_tok = own ? half_bits_to_float(r.nk) * kscale : 0.f;
-        const float nv = half_bits_to_float(r.nv) * inv_sqrt_d;
+        float ks_tok, nv;
+        if constexpr (BN) {
+            ks_tok = own ? kscale : 0.f;
+            nv = max_norm4(r.nvb[kPasses]) * (1.0f / sqrtf(32.f));
+        } else {
+            ks_tok = own ? half_bits_to_float(r.nk) * kscale : 0.f;
+            nv = half_bits_to_float(r.nv) * inv_sqrt_d;
+        }
         float s[kG], p[kG];
         bool over = false;
 #pragma unroll
@@ -561,6 +643,23 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
                     o[p] = *reinterpret_cast<const uint32_t *>(tab_bytes + byte3_pair_offset(sh, p, lane_off | 128u));
             } else {
                 unpack_block<VB>(vlut, r.vw[hp], o);
+            }
+            if constexpr (BN) {
+                // this lane's block over its token's largest block norm
+                const u32x2 nb = r.nvb[hp];
+                const int blk = (lane >> 2) & 3;
+                const float nref = max_norm4(nb);
+                const uint32_t w = blk < 2 ? nb.x : nb.y;
+                const float nbk = half_bits_to_float(static_cast<uint16_t>((blk & 1) ? (w >> 16) : (w & 0xFFFFu)));
+                const _Float16 rt = static_cast<_Float16>(nref > 0.f ? nbk / nref : 0.f);
+                half2v r2 = {rt, rt};
+#pragma unroll
+                for (int p = 0; p < 16; ++p) {
+                    half2v v2;
+                    __builtin_memcpy(&v2, &o[p], 4);
+                    v2 = v2 * r2;
+                    __builtin_memcpy(&o[p], &v2, 4);
+                }
             }
             const half4 aw = tr_read4(ptile, kPass * hp * 8 + p_off);
             // all 8 transposes first, then the products: each product reads a
@@ -652,7 +751,13 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
 template <int KB, int VB, bool QJL>
 hipError_t launch_t(const dev_tables & kt, const dev_tables & vt, const attend_args & a, hipStream_t s) {
     const dim3 grid(a.n_chunks, a.Hkv, a.B);
-    hipLaunchKernelGGL((attend_mfma_kernel<KB, VB, QJL>), grid, dim3(256), 0, s, kt, vt, a);
+    if constexpr (!QJL) {
+        if (kt.norm_group) {
+            hipLaunchKernelGGL((attend_mfma_kernel<KB, VB, false, true>), grid, dim3(256), 0, s, kt, vt, a);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((attend_mfma_kernel<KB, VB, QJL, false>), grid, dim3(256), 0, s, kt, vt, a);
     return hipGetLastError();
 }
 
@@ -666,26 +771,27 @@ hipError_t launch_kb(const dev_tables & kt, const dev_tables & vt, const attend_
     return hipErrorInvalidValue;
 }
 
-template <int KB, int VB, bool QJL>
+template <int KB, int VB, bool QJL, bool BN>
 int slots_t() {
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attend_mfma_kernel<KB, VB, QJL>, 256, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attend_mfma_kernel<KB, VB, QJL, BN>, 256, 0) != hipSuccess)
         per_cu = 1;
     return per_cu;
 }
 
-template <int KB, bool QJL>
+template <int KB, bool QJL, bool BN>
 int slots_kb(int vb) {
-    return vb == 2 ? slots_t<KB, 2, QJL>() : vb == 3 ? slots_t<KB, 3, QJL>() : slots_t<KB, 4, QJL>();
+    return vb == 2 ? slots_t<KB, 2, QJL, BN>() : vb == 3 ? slots_t<KB, 3, QJL, BN>() : slots_t<KB, 4, QJL, BN>();
 }
 
 }  // namespace
 
 int attend_mfma_blocks_per_cu(const dev_tables & kt, const dev_tables & vt) {
+    const bool bn = kt.norm_group != 0;
     switch (kt.bits) {
-        case 2: return kt.qjl ? slots_kb<2, true>(vt.bits) : slots_kb<2, false>(vt.bits);
-        case 3: return kt.qjl ? slots_kb<3, true>(vt.bits) : slots_kb<3, false>(vt.bits);
-        case 4: return kt.qjl ? slots_kb<4, true>(vt.bits) : slots_kb<4, false>(vt.bits);
+        case 2: return kt.qjl ? slots_kb<2, true, false>(vt.bits) : bn ? slots_kb<2, false, true>(vt.bits) : slots_kb<2, false, false>(vt.bits);
+        case 3: return kt.qjl ? slots_kb<3, true, false>(vt.bits) : bn ? slots_kb<3, false, true>(vt.bits) : slots_kb<3, false, false>(vt.bits);
+        case 4: return kt.qjl ? slots_kb<4, true, false>(vt.bits) : bn ? slots_kb<4, false, true>(vt.bits) : slots_kb<4, false, false>(vt.bits);
     }
     return 1;
 }
@@ -693,10 +799,11 @@ int attend_mfma_blocks_per_cu(const dev_tables & kt, const dev_tables & vt) {
 int attend_mfma_chunk_quantum() { return 4 * kStep; }
 
 bool attend_mfma_shape_ok(const dev_tables & kt, const dev_tables & vt, int32_t Hq, int32_t Hkv) {
-    // one norm per vector (block norms take the general kernel); a dense
-    // rotation only with MSE-only keys (its queries come prepared)
-    return kt.d == kD && vt.d == kD && Hq == kG * Hkv && (!kt.qjl || kt.m == kD) && !kt.norm_group &&
-           !vt.norm_group && (!kt.haar || !kt.qjl);
+    // keys and values both with one norm per vector, or both per 32-code
+    // block; a dense rotation only with MSE-only keys (its queries come
+    // prepared)
+    return kt.d == kD && vt.d == kD && Hq == kG * Hkv && (!kt.qjl || kt.m == kD) && kt.norm_group == vt.norm_group &&
+           (!kt.haar || !kt.qjl);
 }
 
 bool attend_mfma_supported(const dev_tables & kt, const dev_tables & vt, const attend_args & a) {

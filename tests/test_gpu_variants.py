@@ -91,8 +91,8 @@ def _oracle_planes(x, cfg):
     return {k: out[k] for k in ("codes", "norms", "signs", "rnorms") if k in out}
 
 
-@pytest.mark.parametrize("kvar,vvar", [("block", "block"), ("block_corr", "corr"), ("haar", "haar"),
-                                       ("haar_corr", "haar"), ("corr", "block")])
+@pytest.mark.parametrize("kvar,vvar", [("block", "block"), ("block_corr", "block"), ("block_corr", "corr"),
+                                       ("haar", "haar"), ("haar_corr", "haar"), ("corr", "block")])
 @pytest.mark.parametrize("d,G", [(64, 4), (128, 4), (128, 1), (256, 2)])
 def test_variant_attend_matches_oracle(kvar, vvar, d, G):
     if VARIANTS[kvar].get("rotation") != VARIANTS[vvar].get("rotation"):
