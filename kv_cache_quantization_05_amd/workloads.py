@@ -21,6 +21,8 @@ are not available, so these distributions stand in for real K/V):
                    values turbo4.
   llama_b4_t128k   B=4, T=131072, as llama_t32k plus 1% of the positions of
                    each batch (same for K, V and all heads) scaled x8; turbo3.
+  llama_t32k_turbo2, llama_t32k_k4v2  as llama_t32k with 2-bit keys and
+                   values, or 4-bit keys and 2-bit values.
   llama_t32k_block32  as llama_t32k with one fp16 norm per 32-code block
                    and norm correction (3.5 bits per value at turbo3).
   llama_t32k_haar  as llama_t32k with the dense seeded Haar rotation.
@@ -77,6 +79,12 @@ WORKLOADS = {
                               outliers=4),
     "llama_b4_t128k": Workload("llama_b4_t128k", 4, 131072, 8, 32, 128, 3, 3, False, "bf16",
                                outliers=4, spike_frac=0.01),
+    # bit-width variants of the 32K layer: turbo2, and asymmetric turbo4 keys
+    # with turbo2 values
+    "llama_t32k_turbo2": Workload("llama_t32k_turbo2", 1, 32768, 8, 32, 128, 2, 2, False, "bf16",
+                                  outliers=4),
+    "llama_t32k_k4v2": Workload("llama_t32k_k4v2", 1, 32768, 8, 32, 128, 4, 2, False, "bf16",
+                                outliers=4),
     # layout and rotation variants of the 32K layer
     "llama_t32k_block32": Workload("llama_t32k_block32", 1, 32768, 8, 32, 128, 3, 3, False, "bf16",
                                    outliers=4, norm_group=32, norm_correction=True),
