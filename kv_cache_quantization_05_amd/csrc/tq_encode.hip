@@ -168,15 +168,6 @@ __global__ __launch_bounds__(256) void encode_kernel(const dev_tables t, const e
     }
 }
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f16x8 as_f16x8(uint4 w) {
-    f16x8 r;
-    __builtin_memcpy(&r, &w, 16);
-    return r;
-}
-
 // QJL ctx.  Phase A (per lane, one 32-coordinate block of one vector): the
 // rotation, z, codes, residual r = z - c[code] and gamma = ||r|| / sqrt(d) in
 // double (so gamma's fp16 rounding matches float64); r goes to LDS as an
@@ -360,47 +351,6 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(const dev_tables t, con
 // l%16.  The A rows are permuted so that the same lane receives output
 // coordinates 8(l/16)..+7 of each block: the cross-block transform, the
 // quantiser and the packing of 8 codes all stay in the lane.
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) {
-    bf16x2 r;
-    __builtin_memcpy(&r, &w, 4);
-    return r;
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(const uint32_t (&w)[4]) {
-    bf16x8 r;
-    __builtin_memcpy(&r, w, 16);
-    return r;
-}
-
-// The value unchanged, but opaque to the optimiser: what is computed from it
-// inside a rarely taken branch stays there instead of being hoisted into the
-// common path.  (An empty asm: no instruction is emitted.)
-__device__ __forceinline__ uint32_t opaque(uint32_t v) {
-    asm volatile("" : "+v"(v));
-    return v;
-}
-
-// 2c + bit, as one add-with-carry whose carry-in is the (per-lane) bit
-__device__ __forceinline__ uint32_t dbl_add(uint32_t c, bool bit) {
-    unsigned int co;
-    return __builtin_addc(c, c, bit ? 1u : 0u, &co);
-}
-
-// 2c + bit with the bits of all lanes given as a wave mask (a compare result,
-// possibly combined with others by scalar logic): one v_addc whose carry-in
-// is the mask, where the compiler would turn each bit into a select and a
-// shift-or.  (A plain ALU instruction: no memory access in the asm.)
-__device__ __forceinline__ uint32_t shift_in(uint32_t c, uint64_t bits) {
-    uint32_t r;
-    uint64_t carry_out;
-    asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(c), "s"(bits));
-    return r;
-}
-
 // At most 128 VGPRs (4 waves per SIMD; no spills): at 130 the prefetching
 // kernel would drop to 3 waves and to the slower non-prefetching launch plan.
 template <int D, int BITS, bool PREFETCH, bool FLAT>
@@ -647,42 +597,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
     }
 }
 
-// The grid folded into one dimension when its vectors are evenly spaced in
-// both the input and the planes (size-1 dimensions dropped, each remaining
-// dimension's strides equal to the folded inner block's extent), with both
-// strides in [0, 2^32).  Returns false, leaving f unset, otherwise.
-bool fold_flat(const encode_args & a, encode_args & f) {
-    const int64_t n[3] = {a.n0, a.n1, a.n2}, xs[3] = {a.xs0, a.xs1, a.xs2};
-    const int64_t ps[3] = {a.out.stride[0], a.out.stride[1], a.out.stride[2]};
-    constexpr int64_t kLim = int64_t(1) << 32;
-    int64_t cn = 1, cx = 0, cp = 0;  // cn < 2^32: the host has checked n0 n1 n2 < 2^32
-    bool any = false;
-    for (int i = 2; i >= 0; --i) {
-        if (n[i] == 1) continue;
-        if (!any) {
-            if (xs[i] < 0 || xs[i] >= kLim || ps[i] < 0 || ps[i] >= kLim) return false;
-            cn = n[i];
-            cx = xs[i];
-            cp = ps[i];
-            any = true;
-        } else {
-            // cn, cx, cp < 2^32: the products fit in 64 unsigned bits
-            if (xs[i] < 0 || ps[i] < 0 || uint64_t(xs[i]) != uint64_t(cn) * uint64_t(cx) ||
-                uint64_t(ps[i]) != uint64_t(cn) * uint64_t(cp))
-                return false;
-            cn *= n[i];
-        }
-    }
-    f = a;
-    f.n0 = f.n1 = 1;
-    f.n2 = cn;
-    f.xs0 = f.xs1 = 0;
-    f.xs2 = cx;
-    f.out.stride[0] = f.out.stride[1] = 0;
-    f.out.stride[2] = cp;
-    return true;
-}
-
 template <int D, int BITS, bool QJL>
 hipError_t launch_encode_dtype(const dev_tables & t, const encode_args & a, uint32_t nvec, hipStream_t s) {
     constexpr int VPB = 256 / (D / 32);
@@ -760,6 +674,7 @@ bool encode_grid_supported(const encode_args & a) {
 hipError_t launch_encode(const dev_tables & t, const encode_args & a, hipStream_t s) {
     if (t.haar || t.norm_group || t.norm_corr) return launch_encode_variant(t, a, s);
     const uint32_t nvec = static_cast<uint32_t>(a.n0 * a.n1 * a.n2);
+    if (encode_qjl_mfma_supported(t, a)) return launch_encode_qjl_mfma(t, a, nvec, s);
     switch (t.d) {
         case 32: return launch_encode_d<32>(t, a, nvec, s);
         case 64: return launch_encode_d<64>(t, a, nvec, s);

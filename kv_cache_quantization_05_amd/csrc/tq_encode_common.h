@@ -1,5 +1,6 @@
 // Helpers shared by the encode kernels: grid indexing, lane-per-block
-// Walsh-Hadamard butterflies, input loads and the symmetric quantiser.
+// Walsh-Hadamard butterflies, input loads, the symmetric quantiser,
+// matrix-core operand casts and the host-side grid folding.
 #pragma once
 
 #include "tq_device.h"
@@ -149,6 +150,87 @@ __device__ __forceinline__ double flip_sign(double v, uint32_t w, int e) {
     const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
     const uint64_t m = static_cast<uint64_t>((w << (31 - e)) & 0x80000000u) << 32;
     return __longlong_as_double(static_cast<long long>(b ^ m));
+}
+
+// Matrix-core operand types and bit-casts.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f16x8 as_f16x8(uint4 w) {
+    f16x8 r;
+    __builtin_memcpy(&r, &w, 16);
+    return r;
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) {
+    bf16x2 r;
+    __builtin_memcpy(&r, &w, 4);
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint32_t (&w)[4]) {
+    bf16x8 r;
+    __builtin_memcpy(&r, w, 16);
+    return r;
+}
+
+// The value unchanged, but opaque to the optimiser: what is computed from it
+// inside a rarely taken branch stays there instead of being hoisted into the
+// common path.  (An empty asm: no instruction is emitted.)
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// 2c + bit with the bits of all lanes given as a wave mask (a compare result,
+// possibly combined with others by scalar logic): one v_addc whose carry-in
+// is the mask, where the compiler would turn each bit into a select and a
+// shift-or.  (A plain ALU instruction: no memory access in the asm.)
+__device__ __forceinline__ uint32_t shift_in(uint32_t c, uint64_t bits) {
+    uint32_t r;
+    uint64_t carry_out;
+    asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(c), "s"(bits));
+    return r;
+}
+
+// The grid folded into one dimension when its vectors are evenly spaced in
+// both the input and the planes (size-1 dimensions dropped, each remaining
+// dimension's strides equal to the folded inner block's extent), with both
+// strides in [0, 2^32).  Returns false, leaving f unset, otherwise.
+inline bool fold_flat(const encode_args & a, encode_args & f) {
+    const int64_t n[3] = {a.n0, a.n1, a.n2}, xs[3] = {a.xs0, a.xs1, a.xs2};
+    const int64_t ps[3] = {a.out.stride[0], a.out.stride[1], a.out.stride[2]};
+    constexpr int64_t kLim = int64_t(1) << 32;
+    int64_t cn = 1, cx = 0, cp = 0;  // cn < 2^32: the host has checked n0 n1 n2 < 2^32
+    bool any = false;
+    for (int i = 2; i >= 0; --i) {
+        if (n[i] == 1) continue;
+        if (!any) {
+            if (xs[i] < 0 || xs[i] >= kLim || ps[i] < 0 || ps[i] >= kLim) return false;
+            cn = n[i];
+            cx = xs[i];
+            cp = ps[i];
+            any = true;
+        } else {
+            // cn, cx, cp < 2^32: the products fit in 64 unsigned bits
+            if (xs[i] < 0 || ps[i] < 0 || uint64_t(xs[i]) != uint64_t(cn) * uint64_t(cx) ||
+                uint64_t(ps[i]) != uint64_t(cn) * uint64_t(cp))
+                return false;
+            cn *= n[i];
+        }
+    }
+    f = a;
+    f.n0 = f.n1 = 1;
+    f.n2 = cn;
+    f.xs0 = f.xs1 = 0;
+    f.xs2 = cx;
+    f.out.stride[0] = f.out.stride[1] = 0;
+    f.out.stride[2] = cp;
+    return true;
 }
 
 }  // namespace

@@ -65,6 +65,10 @@ hipError_t launch_encode(const dev_tables & t, const encode_args & a, hipStream_
 // Haar rotation, block norms or norm correction (tq_encode_var.hip).
 hipError_t launch_encode_variant(const dev_tables & t, const encode_args & a, hipStream_t s);
 bool encode_grid_supported(const encode_args & a);  // n0*n1*n2 < 2^32
+// QJL keys, bf16 input, d = 64 or 128: matrix-core rotation and sketch
+// (tq_encode_qjl.hip).
+bool encode_qjl_mfma_supported(const dev_tables & t, const encode_args & a);
+hipError_t launch_encode_qjl_mfma(const dev_tables & t, const encode_args & a, uint32_t nvec, hipStream_t s);
 
 // Query preparation: qp[i] = [ R q_i (d floats) | S R q_i (m floats, qjl) ].
 hipError_t launch_query_prep(const dev_tables & t, const float * q, int64_t n, float * qp,

@@ -168,6 +168,32 @@ def test_encode_exact_ties_at_zero(d, bits, qjl, dtype):
     _say("tie entries", int(tie.sum()), "tie choices that differ", int(((g_code != ref["code"]) & tie).sum()), rep)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_encode_qjl_wide_dynamic_range(d, bits):
+    # bf16 QJL keys whose coordinates reach more than 2^19 below their
+    # largest one (most of the 24,000 vectors): the matrix-core rotation then
+    # needs its third exponent band, and about 2 to 20 residual norms per case
+    # lie close enough to an fp16 rounding midpoint that the float64
+    # butterflies decide them.  Everything is compared with the oracle.
+    _say("encode wide range", d, bits)
+    ctx = tq.Context(seed=21 + d, head_dim=d, bits=bits, qjl=True)
+    g = torch.Generator().manual_seed(500 + d + bits)
+    n = 24_000
+    x = torch.randn((n, d), generator=g)
+    big = torch.rand((n, d), generator=g) < 0.04          # a few large coordinates
+    x = torch.where(big, x * 2.0 ** 12, x)
+    tiny = torch.rand((n, d), generator=g) < 0.02         # and some far below them
+    x = torch.where(tiny, x * 2.0 ** -10, x)
+    x[:50] = torch.randn((50, d), generator=g) * 1e-3    # and some ordinary vectors
+    x = x.to(torch.bfloat16)
+    planes = tq.encode(ctx, x.to(DEV))
+    torch.cuda.synchronize()
+    cfg = oracle_config(ctx)
+    ref = oenc.encode(x.float().numpy().astype(np.float64), cfg)
+    _say(compare_encode(planes.numpy(), ref, cfg))
+
+
 def test_encode_empty_grid_is_noop():
     ctx = tq.Context(seed=0, head_dim=128, bits=3)
     x = torch.zeros((0, 128), device=DEV)
