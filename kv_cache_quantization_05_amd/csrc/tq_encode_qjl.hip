@@ -380,11 +380,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
         for (int j = 0; j < 8; ++j) T[j] = p[j] * nf;
         uint32_t cpre[NB];  // [sign, magnitude] code fields before the XORs
         double gsqb[NB];  // one partial sum per block
-        // the sketch h = S D1 r' accumulates block by block (k-step bo takes
-        // block bo's residual), so its products overlap the next block's work
-        f32x4 hacc[RT];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) hacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        uint32_t rh[NB][4], rl[NB][4];  // the residual as fp16 hi + lo pairs
         const bool any_zero = __any(nv == 0.0);
         uint8_t * const crow = a.out.codes + pv * (D * BITS / 8);
         // each 8-code chunk is built bit-serially from the top: the sign bit,
@@ -436,9 +432,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
                 rf[j] = static_cast<float>(r);
             }
             gsqb[bo] = g0 + g1;
-            uint32_t rh[4], rl[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) split_pair(rf[2 * k], rf[2 * k + 1], rh[k], rl[k]);
+            for (int k = 0; k < 4; ++k) split_pair(rf[2 * k], rf[2 * k + 1], rh[bo][k], rl[bo][k]);
             // a zero vector: every z is 0, its code 2^(b-1) - 1 and r = +c_pos[0]
             // in every coordinate, i.e. r' = D1 c_pos[0] here
             if (any_zero) {
@@ -447,22 +442,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
                     const uint32_t d1b = opaque(t.d1[bo] >> (8 * g));
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
-                        rh[k] = (c0 ^ (((d1b >> (2 * k)) & 1u) << 15)) | ((c0 ^ (((d1b >> (2 * k + 1)) & 1u) << 15)) << 16);
-                        rl[k] = 0;
+                        rh[bo][k] = (c0 ^ (((d1b >> (2 * k)) & 1u) << 15)) | ((c0 ^ (((d1b >> (2 * k + 1)) & 1u) << 15)) << 16);
+                        rl[bo][k] = 0;
                     }
-                }
-            }
-            {
-                // three fp16 products per row tile: hi hi, hi lo, lo hi
-                const f16x8 bh = as_f16x8(uint4{rh[0], rh[1], rh[2], rh[3]});
-                const f16x8 bl = as_f16x8(uint4{rl[0], rl[1], rl[2], rl[3]});
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    const f16x8 ah = as_f16x8(sfrag[((rt * NB + bo) * 2) * 64 + lane]);
-                    const f16x8 al = as_f16x8(sfrag[((rt * NB + bo) * 2 + 1) * 64 + lane]);
-                    hacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, hacc[rt], 0, 0, 0);
-                    hacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl, hacc[rt], 0, 0, 0);
-                    hacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, hacc[rt], 0, 0, 0);
                 }
             }
             {
@@ -557,6 +539,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
             if (!g_ok) gbits = half_bits_rne(sqrt(gs * (1.0 / D)));
         }
 
+        // sketch h = S D1 r': three fp16 products per row tile and k-step (hi
+        // hi, hi lo, lo hi), the A fragments loaded kPipe steps ahead of their
+        // products (the scheduling barrier keeps the compiler from sinking each
+        // load to just before its use, which exposes the LDS latency)
+        constexpr int NS = NB * RT, kPipe = 4;
+        f32x4 hacc[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) hacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto frag = [&](int st, int part) {
+            return as_f16x8(sfrag[(((st % RT) * NB + st / RT) * 2 + part) * 64 + lane]);
+        };
+        f16x8 fh[kPipe], fl[kPipe];
+#pragma unroll
+        for (int st = 0; st < kPipe; ++st) {
+            fh[st] = frag(st, 0);
+            fl[st] = frag(st, 1);
+        }
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            const int ks = st / RT, rt = st % RT;
+            const f16x8 ah = fh[st % kPipe], al = fl[st % kPipe];
+            if (st + kPipe < NS) {
+                fh[st % kPipe] = frag(st + kPipe, 0);
+                fl[st % kPipe] = frag(st + kPipe, 1);
+            }
+            const f16x8 bh = as_f16x8(uint4{rh[ks][0], rh[ks][1], rh[ks][2], rh[ks][3]});
+            const f16x8 bl = as_f16x8(uint4{rl[ks][0], rl[ks][1], rl[ks][2], rl[ks][3]});
+            hacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, hacc[rt], 0, 0, 0);
+            hacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl, hacc[rt], 0, 0, 0);
+            hacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, hacc[rt], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         // lane (n, g) holds rows 4 RT g + 4 rt + i: bit 4 rt + i of its sign word
         // (the sign bit of h, inverted: set for h >= +0)
         uint32_t sgn = 0;
