@@ -340,17 +340,15 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(const dev_tables t, con
 // bf16 input, MSE-only, d = 64 or 128: the rotation on matrix cores.
 //
 // H_d = H_(d/32) (x) H_32 (Sylvester order: the block index is the high bits
-// of the coordinate), so H_d D2 x is a 32-point transform of every block,
-// u_b = H_32 (D2 x)_b, followed by an (d/32)-point transform across blocks.
-// The 32-point part is a 16x16x32 bf16 MFMA per block and 16-row half, with
-// the inputs as the B operand exactly as loaded (bf16) and the +-1 entries
-// of H_32 D2_b as the A operand (D2 and the cross-block signs folded into
-// the tiles): products are exact and the sums accumulate in fp32, as in the
-// VALU butterflies.  A wave takes 16
-// vectors; lane l loads coordinates 8(l/16)..+7 of each block of vector
-// l%16.  The A rows are permuted so that the same lane receives output
-// coordinates 8(l/16)..+7 of each block: the cross-block transform, the
-// quantiser and the packing of 8 codes all stay in the lane.
+// of the coordinate), so output block b' of H_d D2 x is the sum over input
+// blocks b of (-1)^popcount(b' & b) H_32 (D2 x)_b.  Each term is a 16x16x32
+// bf16 MFMA per 16-row half, accumulated over b in fp32: the B operand is
+// the input with D2's sign flips (bf16, exact), the A operand the +-1
+// entries of +-H_32, so the products are exact.  A wave takes 16 vectors;
+// lane l loads coordinates 8(l/16)..+7 of each block of vector l%16.  The A
+// rows are permuted so that the same lane receives output coordinates
+// 8(l/16)..+7 of each block: the quantiser and the packing of 8 codes stay
+// in the lane.
 // At most 128 VGPRs (4 waves per SIMD; no spills): at 130 the prefetching
 // kernel would drop to 3 waves and to the slower non-prefetching launch plan.
 template <int D, int BITS, bool PREFETCH, bool FLAT>
@@ -393,22 +391,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
             const int e = 8 * g + 2 * j;
             m2[b][j] = (((t.d2[b] >> e) & 1) << 15) | (((t.d2[b] >> (e + 1)) & 1) << 31);
         }
-    // D2 folded into the A operand's columns: tile (tt, bi, s) is
-    // (-1)^s H_32 D2_bi, so the B operand is the input exactly as loaded
-    bf16x8 hA[2][NB][2];
+    // A operand tiles (-1)^s H_32; D2 is applied to the input by sign-bit
+    // XORs (16 registers of tiles instead of 64 with D2 folded in: five
+    // waves per SIMD for the non-prefetching kernel)
+    bf16x8 hA[2][2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int bi = 0; bi < NB; ++bi) {
-            uint32_t p[4], m[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                p[j] = hw[tt][j] ^ m2[bi][j];
-                m[j] = hwn[tt][j] ^ m2[bi][j];
-            }
-            hA[tt][bi][0] = as_bf16x8(p);
-            hA[tt][bi][1] = as_bf16x8(m);
-        }
+    for (int tt = 0; tt < 2; ++tt) {
+        hA[tt][0] = as_bf16x8(hw[tt]);
+        hA[tt][1] = as_bf16x8(hwn[tt]);
+    }
     // D1 (all bits of a code whose z changes sign) as XORs of the lane's
     // 8-code chunks; and the chunk of a zero vector
     uint32_t xm[NB], zero_chunk = 0;
@@ -453,12 +444,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
         if (!PREFETCH) load_inputs(base);
         const bool valid = valid_next;
         const int64_t pv = pv_next;
-        // the inputs as loaded (D2 sits in the A operand)
+        // D2 x: sign flips of the loaded bf16 pairs
         uint32_t w[NB][4];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) w[b][j] = wn[b][j];
+            for (int j = 0; j < 4; ++j) w[b][j] = wn[b][j] ^ m2[b][j];
         if (PREFETCH) load_inputs(base + stride);
 
         // Norm, as float64 rounds it to fp16.  First in fp32 from exact bf16
@@ -542,7 +533,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int bi = 0; bi < NB; ++bi)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hA[tt][bi][__builtin_popcount(b & bi) & 1], xb[bi], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hA[tt][__builtin_popcount(b & bi) & 1], xb[bi], acc, 0, 0, 0);
                 u[tt] = acc;
             }
             // each 8-code chunk is built bit-serially from the top: the sign
