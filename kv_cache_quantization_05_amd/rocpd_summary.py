@@ -37,7 +37,7 @@ GIB = 1 << 30
 GROUPS = {
     "attend_decode": re.compile(r"attend_mfma_kernel|attend_partial_kernel|attend_merge_kernel|query_prep_kernel"),
     "attend_prefill": re.compile(r"prefill_kernel|rotate_back_kernel"),
-    "encode": re.compile(r"encode_kernel|encode_qjl_kernel|encode_mfma_kernel|encode_var_kernel|encode_haar_kernel"),
+    "encode": re.compile(r"encode_kernel|encode_qjl_kernel|encode_qjl_mfma_kernel|encode_mfma_kernel|encode_var_kernel|encode_haar_kernel"),
     "scores": re.compile(r"scores_mfma_kernel|scores_topk_kernel|scores_full_kernel|topk_merge_kernel"),
 }
 # dispatches that count launches of each group
