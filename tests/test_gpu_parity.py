@@ -93,6 +93,32 @@ def test_encode_strided_grid_into_cache_layout():
     assert np.all(got["codes"][:, :, T:] == 0) and np.all(got["norms"][:, :, T:] == 0)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_encode_qjl_strided_grid_into_cache_layout(d):
+    # bf16 QJL keys laid out [B, T, Hkv, d] (prefill order), read as a strided
+    # [B, Hkv, T] grid and written into [B, Hkv, Tcap] planes: the grid
+    # cannot be folded, and codes, norms, signs and residual norms land at
+    # strided plane positions; the rest of the planes stays untouched
+    _say("encode qjl strided", d)
+    ctx = tq.Context(seed=2, head_dim=d, bits=4, qjl=True)
+    B, T, Hkv, Tcap = 2, 100, 4, 160
+    x = _x((B, T, Hkv, d), torch.bfloat16, seed=30 + d).to(DEV)
+    planes = ctx.new_planes((B, Hkv, Tcap))
+    for t in (planes.codes, planes.norms, planes.signs, planes.rnorms):
+        t.zero_()
+    view = tq.PackedPlanes(planes.codes[:, :, :T], planes.norms[:, :, :T], planes.signs[:, :, :T],
+                           planes.rnorms[:, :, :T])
+    tq.encode(ctx, x.permute(0, 2, 1, 3), view)
+    torch.cuda.synchronize()
+    cfg = oracle_config(ctx)
+    ref = oenc.encode(x.permute(0, 2, 1, 3).float().cpu().numpy().astype(np.float64), cfg)
+    got = planes.numpy()
+    sub = {k: got[k][:, :, :T] for k in ("codes", "norms", "signs", "rnorms")}
+    _say(compare_encode(sub, ref, cfg))
+    for k in ("codes", "norms", "signs", "rnorms"):
+        assert np.all(got[k][:, :, T:] == 0), k
+
+
 @pytest.mark.parametrize("d,bits,strided", [(64, 4, False), (128, 3, False), (128, 3, True)])
 def test_encode_many_vectors(d, bits, strided):
     # more vectors than a few rounds of resident blocks cover, so the encoder
@@ -172,14 +198,15 @@ def test_encode_exact_ties_at_zero(d, bits, qjl, dtype):
 @pytest.mark.parametrize("bits", [2, 3, 4])
 def test_encode_qjl_wide_dynamic_range(d, bits):
     # bf16 QJL keys whose coordinates reach more than 2^19 below their
-    # largest one (most of the 24,000 vectors): the matrix-core rotation then
-    # needs its third exponent band, and about 2 to 20 residual norms per case
-    # lie close enough to an fp16 rounding midpoint that the float64
-    # butterflies decide them.  Everything is compared with the oracle.
+    # largest one (most of the 40,000 vectors, more than one round of the
+    # resident grid): the matrix-core rotation then needs its third exponent
+    # band, and a few residual norms per case lie close enough to an fp16
+    # rounding midpoint that the float64 butterflies decide them.  Everything
+    # is compared with the oracle.
     _say("encode wide range", d, bits)
     ctx = tq.Context(seed=21 + d, head_dim=d, bits=bits, qjl=True)
     g = torch.Generator().manual_seed(500 + d + bits)
-    n = 24_000
+    n = 40_000
     x = torch.randn((n, d), generator=g)
     big = torch.rand((n, d), generator=g) < 0.04          # a few large coordinates
     x = torch.where(big, x * 2.0 ** 12, x)
