@@ -44,17 +44,20 @@ __global__ __launch_bounds__(256) void query_prep_kernel(const dev_tables t, con
     const int k = threadIdx.x;
     float y;
     if (t.haar) {
-        // dense rotation: q'_k = sum_j Q_kj q_j ([TQ+ guide] §4, the O(d^2) form)
+        // dense rotation: q'_k = sum_j Q_kj q_j ([TQ+ guide] §4, the O(d^2) form);
+        // the row's loads all issued at once and four partial sums (the
+        // launch is a few dozen blocks: latency, not bandwidth, sets its time)
         s[k] = q[i * D + k];
         __syncthreads();
         const float4 * row = reinterpret_cast<const float4 *>(t.Q + int64_t(k) * D);
-        float acc = 0.f;
-#pragma unroll 4
-        for (int j = 0; j < D / 4; ++j) {
-            const float4 r = row[j];
-            acc = fmaf(r.x, s[4 * j], fmaf(r.y, s[4 * j + 1], fmaf(r.z, s[4 * j + 2], fmaf(r.w, s[4 * j + 3], acc))));
-        }
-        y = acc;
+        float4 r[D / 4];
+#pragma unroll
+        for (int j = 0; j < D / 4; ++j) r[j] = row[j];
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < D / 4; ++j)
+            acc[j & 3] = fmaf(r[j].x, s[4 * j], fmaf(r[j].y, s[4 * j + 1], fmaf(r[j].z, s[4 * j + 2], fmaf(r[j].w, s[4 * j + 3], acc[j & 3]))));
+        y = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     } else {
         float x = q[i * D + k];
         if ((t.d2[k >> 5] >> (k & 31)) & 1) x = -x;
@@ -338,7 +341,6 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(const dev_tables vt, 
 #pragma unroll
     for (int i = 0; i < PER; ++i) wacc[wave][lane + 64 * i] = acc[i];
     __syncthreads();
-    if (wave != 0) return;
     const float Mx = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
     float sw[4], L = 0.f;
 #pragma unroll
@@ -350,29 +352,61 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(const dev_tables vt, 
     const float inv = ok ? 1.0f / L : 0.f;
     if (vt.haar) {
         // dense rotation: o = Q^T o'  ([TQ+ guide] §6.1, rotated back with
-        // the value context's rotation); o' staged in LDS, column reads of Q
+        // the value context's rotation).  o' staged in LDS by wave 0; each wave
+        // then sums a quarter of the rows j for every output dim, its loads all
+        // issued at once (a serial pass over j was latency-bound), and wave 0
+        // adds the four parts.
+        if (wave == 0) {
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int dim = lane + 64 * i;
-            if (dim < D) {
-                float o = 0.f;
+            for (int i = 0; i < PER; ++i) {
+                const int dim = lane + 64 * i;
+                if (dim < D) {
+                    float o = 0.f;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) o = fmaf(sw[w], wacc[w][dim], o);
-                ost[dim] = o * inv;
+                    for (int w = 0; w < 4; ++w) o = fmaf(sw[w], wacc[w][dim], o);
+                    ost[dim] = o * inv;
+                }
             }
         }
-        __threadfence_block();  // this wave's LDS writes land before its reads
+        __syncthreads();
+        constexpr int JW = (D + 3) / 4;  // rows per wave
+        float part[PER];
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int dim = lane + 64 * i;
-            if (dim < D) {
-                float o = 0.f;
-                for (int j = 0; j < D; ++j) o = fmaf(vt.Q[int64_t(j) * D + dim], ost[j], o);
-                a.out[(int64_t(b) * a.Hq + h) * D + dim] = o;
+            const int dd = dim < D ? dim : 0;
+            float qv[JW];
+#pragma unroll
+            for (int jj = 0; jj < JW; ++jj) {
+                const int j = wave * JW + jj;
+                qv[jj] = j < D ? vt.Q[int64_t(j) * D + dd] : 0.f;
             }
+            float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < JW; ++jj) {
+                const int j = wave * JW + jj;
+                const float sj = j < D ? ost[j] : 0.f;
+                if (jj & 1)
+                    p1 = fmaf(qv[jj], sj, p1);
+                else
+                    p0 = fmaf(qv[jj], sj, p0);
+            }
+            part[i] = p0 + p1;
+        }
+        __syncthreads();  // every wave has read ost: wacc is reused for the parts
+#pragma unroll
+        for (int i = 0; i < PER; ++i) wacc[wave][lane + 64 * i] = part[i];
+        __syncthreads();
+        if (wave != 0) return;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int dim = lane + 64 * i;
+            if (dim < D)
+                a.out[(int64_t(b) * a.Hq + h) * D + dim] = (wacc[0][dim] + wacc[1][dim]) + (wacc[2][dim] + wacc[3][dim]);
         }
         return;
     }
+    if (wave != 0) return;
     float x[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
