@@ -258,7 +258,7 @@ int64_t tq_scores_workspace(const tq_ctx * k_ctx, int64_t n_q, int64_t n_k, int3
     if (top_k == 0) return qp;
     int32_t ranges = 1;
     int64_t per = 0;
-    tq::scores_plan(k_ctx->tab.d, k_ctx->tab.norm_group != 0, n_q, n_k, ranges, per);
+    tq::scores_plan(k_ctx->tab.d, k_ctx->tab.norm_group != 0, n_q, n_k, top_k, ranges, per);
     return qp + round_up(int64_t(ranges) * n_q * top_k * 4) + round_up(int64_t(ranges) * n_q * top_k * 8);
 }
 
@@ -295,7 +295,7 @@ int32_t tq_scores(const tq_ctx * k_ctx, const float * q, int64_t n_q, float scal
     a.top_k = top_k;
     a.out_scores = out_scores;
     a.out_idx = out_idx;
-    tq::scores_plan(k_ctx->tab.d, k_ctx->tab.norm_group != 0, n_q, n_k, a.n_ranges, a.keys_per_range);
+    tq::scores_plan(k_ctx->tab.d, k_ctx->tab.norm_group != 0, n_q, n_k, top_k, a.n_ranges, a.keys_per_range);
     if (top_k > 0) {
         char * p = ws + round_up(n_q * qp_stride * 4);
         a.cand_s = reinterpret_cast<float *>(p);

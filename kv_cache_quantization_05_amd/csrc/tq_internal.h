@@ -133,7 +133,13 @@ struct scores_args {
     int64_t keys_per_range;     // keys of one range (a multiple of 16 on the matrix-core path)
 };
 hipError_t launch_scores(const dev_tables & t, const scores_args & a, hipStream_t s);
-// Split of the keys into ranges (one block column each) for head_dim d.
-void scores_plan(int d, bool block_norms, int64_t n_q, int64_t n_k, int32_t & ranges, int64_t & keys_per_range);
+// Split of the keys into ranges (one top-k list per query each) for head_dim d.
+void scores_plan(int d, bool block_norms, int64_t n_q, int64_t n_k, int32_t top_k, int32_t & ranges,
+                 int64_t & keys_per_range);
+// 32 x 32-tile scorer (tq_scores32.hip): d = 128 or 256, one norm per vector,
+// top_k <= 16; one wave per range, scores_tile32_waves() ranges per block.
+bool scores_tile32_supported(int d, bool block_norms, int32_t top_k);
+int scores_tile32_waves();
+hipError_t launch_scores_tile32(const dev_tables & t, const scores_args & a, hipStream_t s);
 
 }  // namespace tq

@@ -476,6 +476,12 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(const dev_tables t, co
 
 template <int D, int KB, bool QJL>
 hipError_t launch_scores_t(const dev_tables & t, const scores_args & a, hipStream_t s) {
+    if (scores_tile32_supported(D, t.norm_group != 0, a.top_k)) {
+        hipError_t e = launch_scores_tile32(t, a, s);
+        if (e != hipSuccess || a.top_k == 0) return e;
+        hipLaunchKernelGGL(topk_merge_kernel, dim3(a.n_q), dim3(64), 0, s, a);
+        return hipGetLastError();
+    }
     if constexpr (D >= 128) {
         if (!t.norm_group) {
             const int64_t items = ((a.n_q + 15) / 16 + 3) / 4 * a.n_ranges;
@@ -520,12 +526,30 @@ hipError_t launch_scores_d(const dev_tables & t, const scores_args & a, hipStrea
 
 }  // namespace
 
-// Matrix-core path (d >= 128, one norm per vector): about 4096 waves in all (one per 16 queries
-// and range), at most 256 ranges (the final merge reads up to 4 lists per
-// lane), ranges a multiple of 16 keys.  VALU path: ranges of ~4096 keys.
-void scores_plan(int d, bool block_norms, int64_t n_q, int64_t n_k, int32_t & ranges, int64_t & keys_per_range) {
+// 32 x 32-tile path (d = 128 or 256, one norm per vector, top_k <= 16): one
+// wave per (32 queries, range), about 2048 waves in all (two per SIMD), the
+// ranges a multiple of the waves per block and of 32 keys.  16 x 16-tile path
+// (d >= 128, one norm per vector, larger top_k): about 4096 waves in all (one
+// per 16 queries and range), ranges a multiple of 16 keys.  Both at most 256
+// ranges (the final merge reads up to 4 lists per lane).  VALU path: ranges
+// of ~4096 keys.
+void scores_plan(int d, bool block_norms, int64_t n_q, int64_t n_k, int32_t top_k, int32_t & ranges,
+                 int64_t & keys_per_range) {
     int64_t r;
-    if (d >= 128 && !block_norms) {
+    if (scores_tile32_supported(d, block_norms, top_k)) {
+        const int64_t qtiles = (n_q + 31) / 32;
+        const int64_t w = scores_tile32_waves();
+        r = (2048 + qtiles - 1) / qtiles;
+        r = (r + w - 1) / w * w;
+        const int64_t max_r = (n_k + 31) / 32;
+        if (r > max_r) r = max_r;
+        if (r > 256) r = 256;
+        if (r < 1) r = 1;
+        int64_t per = (n_k + r - 1) / r;
+        per = (per + 31) / 32 * 32;
+        keys_per_range = per;
+        r = (n_k + per - 1) / per;
+    } else if (d >= 128 && !block_norms) {
         const int64_t qtiles = (n_q + 15) / 16;
         r = (4096 + qtiles - 1) / qtiles;
         const int64_t max_r = (n_k + 15) / 16;
