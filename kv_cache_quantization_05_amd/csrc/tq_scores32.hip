@@ -31,14 +31,17 @@
 //      s = scale * N * (<R q, c> / sqrt(d) + gamma sqrt(pi/2) / m <S R q, sigma>)
 //      ([TQ+ guide] §5.3, pre-rotated queries).
 // Top-k ([TQ explainer] §3.4, inner-product search): every wave scans its own
-// key range and keeps, per query, a sorted list in LDS; a final kernel merges
-// the per-range lists (equal scores: lower index first).  The first 32 keys
+// key range and keeps, per query, a sorted list in registers (query
+// 8 i + 4 h + j: register 4 i + j of lanes 32 h .. 32 h + k - 1, one row of
+// 16 lanes, so an insertion is a ballot and a row shift); a final kernel
+// merges the per-range lists (equal scores: lower index first).  The first 32 keys
 // fill the lists by one sort per half-wave.  Afterwards a score enters only
-// if it reaches the workgroup's threshold for its query, the largest k-th
-// best over the eight waves' lists: the k-th best of any subset of the keys
-// is at most the k-th best of all of them, so no key of the final top-k is
-// ever filtered out, and none is evicted from its list (fewer than k keys
-// beat it).
+// if it reaches the workgroup's threshold for its query, a value that at
+// least k distinct keys already reach: the largest k-th best of the eight
+// waves' lists, raised to the smallest c-th best over the lists (c =
+// ceil(k / waves), so at least k keys).  The k-th best of all keys is at least
+// that value, so no key of the final top-k is ever filtered out, and none is
+// evicted from its list (fewer than k keys beat it).
 #include <cmath>
 
 #include "tq_device.h"
@@ -60,21 +63,6 @@ __device__ __forceinline__ half8 as_half8(const uint32_t * w) {
     return h;
 }
 
-// Insert (s, idx) into the sorted list (ls, li) of length K <= 64 (one wave).
-__device__ __forceinline__ void list_insert(float * ls, int32_t * li, int K, float s, int32_t idx, int lane) {
-    const float es = lane < K ? ls[lane] : -INFINITY;
-    const int32_t ei = lane < K ? li[lane] : INT32_MAX;
-    const bool ahead = lane < K && (es > s || (es == s && ei < idx));
-    const int pos = __popcll(__ballot(ahead));
-    const float ps = __shfl_up(es, 1);
-    const int32_t pi = __shfl_up(ei, 1);
-    if (pos < K && lane < K && lane >= pos) {
-        ls[lane] = lane == pos ? s : ps;
-        li[lane] = lane == pos ? idx : pi;
-    }
-    __builtin_amdgcn_wave_barrier();
-}
-
 // 32 sign bits -> 16 dwords of fp16 pairs: pair k = (bit k, bit k + 16) as
 // b 2^(k' - 24), k' = k for k < 10 and k - 6 above (exact fp16 denormals).
 __device__ __forceinline__ void expand_signs(uint32_t bits, uint32_t * out) {
@@ -90,6 +78,9 @@ __host__ __device__ constexpr int sign_shift_of_pos(int pos) { return (pos >> 1)
 __device__ __forceinline__ bool ahead_of(float s1, int32_t i1, float s2, int32_t i2) {
     return s1 > s2 || (s1 == s2 && i1 < i2);
 }
+
+// Lane l - 1's value within each row of 16 lanes (lane 0 of a row: x).
+__device__ __forceinline__ int32_t row_shr1(int32_t x) { return __builtin_amdgcn_update_dpp(x, x, 0x111, 0xF, 0xF, false); }
 
 // Bitonic sort of (s, i) within each 32-lane half of the wave, best first.
 __device__ __forceinline__ void half_sort32(float & s, int32_t & i, int lane) {
@@ -122,11 +113,11 @@ void scores_tile32_kernel(const dev_tables t, const scores_args a) {
     // instructions' offset field; the pair table after them
     constexpr int kFrags = kFrag * (QJL ? 2 : 1);
     __shared__ __align__(16) uint8_t lds_all[kFrags + kTab];
-    __shared__ float lst_s[kWaves][TOPK ? 32 : 1][kCap];
-    __shared__ int32_t lst_i[kWaves][TOPK ? 32 : 1][kCap];
     // the workgroup's thresholds in the lane order of the D operand:
     // thr[h][4 i + j] belongs to query 8 i + 4 h + j
     __shared__ __align__(16) float thr[2][16];
+    // each wave's c-th best per query
+    __shared__ float pub[kWaves][32];
     __shared__ float sum_u[32];
     __shared__ float max_u;
     uint8_t * const frag_lo = lds_all;
@@ -225,12 +216,14 @@ void scores_tile32_kernel(const dev_tables t, const scores_args a) {
             for (int e = 0; e < 8; ++e) aqh[s][e] = static_cast<_Float16>(qrow[dim_of(lane, s, e)]);
     }
     const int K = a.top_k;
+    // c: (waves with a range) * c >= K; a wave without a range takes no part
+    // in the smallest c-th best (its entry stays +inf)
+    const int active = static_cast<int>(a.n_ranges - (item / n_qt) * kWaves < kWaves ? a.n_ranges - (item / n_qt) * kWaves
+                                                                                  : kWaves);
+    const int kc = (K + active - 1) / active;
     if constexpr (TOPK) {
-        for (int i = lane; i < 32 * kCap; i += 64) {
-            lst_s[wave][i / kCap][i % kCap] = -INFINITY;
-            lst_i[wave][i / kCap][i % kCap] = INT32_MAX;
-        }
         if (tid < 32) thr[tid >> 4][tid & 15] = -INFINITY;
+        if (lane < 32) pub[wave][lane] = has_range ? -INFINITY : INFINITY;
     }
     __syncthreads();
 
@@ -243,6 +236,16 @@ void scores_tile32_kernel(const dev_tables t, const scores_args a) {
     float cinit[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) cinit[v] = QJL ? ldexpf(-sum_u[8 * (v >> 2) + 4 * h + (v & 3)], -(E + 1)) : 0.f;
+
+    // top-k lists: entry n of query 8 i + 4 h + j in register 4 i + j of lane
+    // 32 h + n (n < K)
+    float ls[TOPK ? 16 : 1];
+    int32_t li[TOPK ? 16 : 1];
+#pragma unroll
+    for (int v = 0; v < (TOPK ? 16 : 1); ++v) {
+        ls[v] = -INFINITY;
+        li[v] = INT32_MAX;
+    }
 
     // the next 32 keys' codes, signs and norms are loaded while the current
     // ones are scored
@@ -334,10 +337,11 @@ void scores_tile32_kernel(const dev_tables t, const scores_args a) {
                 half_sort32(sv, iv, lane);
                 const int m = 8 * (v >> 2) + 4 * h + (v & 3);
                 if (n32 < K) {
-                    lst_s[wave][m][n32] = sv;
-                    lst_i[wave][m][n32] = iv;
+                    ls[v] = sv;
+                    li[v] = iv;
                 }
                 if (n32 == K - 1) __hip_atomic_fetch_max(&thr[h][v], sv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                if (n32 == kc - 1) pub[wave][m] = sv;
             }
             __builtin_amdgcn_wave_barrier();
         } else {
@@ -361,32 +365,66 @@ void scores_tile32_kernel(const dev_tables t, const scores_args a) {
                 for (int v = 0; v < 16; ++v) {
                     uint64_t mask = __ballot(valid && sc[v] >= th[v]);
                     if (!mask) continue;
+                    // one candidate of each half per round (rows m(v, 0) and
+                    // m(v, 1) are independent lists)
                     while (mask) {
-                        const int src = __builtin_ctzll(mask);
-                        mask &= mask - 1;
-                        const int m = 8 * (v >> 2) + 4 * (src >> 5) + (v & 3);
-                        const float sv = __shfl(sc[v], src);
-                        const int32_t iv = __shfl(static_cast<int32_t>(key), src);
-                        if (sv >= lst_s[wave][m][K - 1]) list_insert(lst_s[wave][m], lst_i[wave][m], K, sv, iv, lane);
+                        const uint32_t mlo = static_cast<uint32_t>(mask), mhi = static_cast<uint32_t>(mask >> 32);
+                        const int s0 = mlo ? __builtin_ctz(mlo) : 0, s1 = mhi ? 32 + __builtin_ctz(mhi) : 32;
+                        if (mlo) mask &= ~(uint64_t(1) << s0);
+                        if (mhi) mask &= ~(uint64_t(1) << s1);
+                        const float c0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc[v]), s0));
+                        const float c1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc[v]), s1));
+                        const int32_t k0 = __builtin_amdgcn_readlane(static_cast<int32_t>(key), s0);
+                        const int32_t k1 = __builtin_amdgcn_readlane(static_cast<int32_t>(key), s1);
+                        const bool has = h ? mhi != 0 : mlo != 0;
+                        const float cs = h ? c1 : c0;
+                        const int32_t ci = h ? k1 : k0;
+                        const bool ahead = n32 < K && (ls[v] > cs || (ls[v] == cs && li[v] < ci));
+                        const uint64_t am = __ballot(ahead);
+                        const int pos = h ? __popc(static_cast<uint32_t>(am >> 32)) : __popc(static_cast<uint32_t>(am));
+                        const float up_s = __int_as_float(row_shr1(__float_as_int(ls[v])));
+                        const int32_t up_i = row_shr1(li[v]);
+                        if (has && n32 < K && n32 >= pos) {
+                            ls[v] = n32 == pos ? cs : up_s;
+                            li[v] = n32 == pos ? ci : up_i;
+                        }
                     }
+                    // publish the k-th and c-th best of both rows
+                    const float kth0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[v]), K - 1));
+                    const float kth1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[v]), 32 + K - 1));
+                    const float cth0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[v]), kc - 1));
+                    const float cth1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[v]), 32 + kc - 1));
                     if (lane < 2) {
                         const int m = 8 * (v >> 2) + 4 * lane + (v & 3);
-                        __hip_atomic_fetch_max(&thr[lane][v], lst_s[wave][m][K - 1], __ATOMIC_RELAXED,
+                        __hip_atomic_fetch_max(&thr[lane][v], lane ? kth1 : kth0, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_WORKGROUP);
+                        pub[wave][m] = lane ? cth1 : cth0;
                     }
-                    __builtin_amdgcn_wave_barrier();
                 }
+            }
+            // queries 4 w .. 4 w + 3: the smallest c-th best over the eight
+            // waves (lane 4 w' + r reads wave w' of query 4 w + r)
+            if (lane < 32) {
+                const int m = 4 * wave + (lane & 3);
+                float c = pub[lane >> 2][m];
+                c = fminf(c, __shfl_xor(c, 4));
+                c = fminf(c, __shfl_xor(c, 8));
+                c = fminf(c, __shfl_xor(c, 16));
+                if (lane < 4)
+                    __hip_atomic_fetch_max(&thr[(m >> 2) & 1][4 * (m >> 3) + (m & 3)], c, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         }
     }
     if constexpr (TOPK) {
         if (has_range) {
-            for (int m = 0; m < 32; ++m) {
-                const int64_t q = q0 + m;
-                if (q < a.n_q && lane < K) {
-                    const int64_t o = (range * a.n_q + q) * K + lane;
-                    a.cand_s[o] = lst_s[wave][m][lane];
-                    a.cand_i[o] = lst_i[wave][m][lane] == INT32_MAX ? INT64_MAX : int64_t(lst_i[wave][m][lane]);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t q = q0 + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (q < a.n_q && n32 < K) {
+                    const int64_t o = (range * a.n_q + q) * K + n32;
+                    a.cand_s[o] = ls[v];
+                    a.cand_i[o] = li[v] == INT32_MAX ? INT64_MAX : int64_t(li[v]);
                 }
             }
         }
