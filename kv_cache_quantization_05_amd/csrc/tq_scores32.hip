@@ -267,6 +267,9 @@ void scores_tile32_kernel(const dev_tables t, const scores_args a) {
     };
     if (k_begin < k_end) load_keys(k_begin);
     for (int64_t j0 = k_begin; j0 < k_end; j0 += 32) {
+        // the LDS fragments are re-read every step, not hoisted into 128
+        // registers for the whole loop
+        asm volatile("" ::: "memory");
         const int64_t key = j0 + n32;
         const bool valid = key < k_end;
         uint32_t w[NBH * KB], sw[QJL ? NBH : 1];
