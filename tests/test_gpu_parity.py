@@ -459,6 +459,55 @@ def test_scores_topk_matches_oracle(k):
     _say("top-k agreement with the oracle's exact list", agree)
 
 
+@pytest.mark.parametrize("d,bits,qjl,k", [(256, 4, True, 10), (256, 4, True, 16), (128, 3, False, 16),
+                                           (256, 4, True, 17)])
+def test_scores_topk_ties_pick_lower_indices(d, bits, qjl, k):
+    """40 distinct vectors, each stored 300 times at scattered positions: equal
+    keys give bit-equal scores, so within the GPU's list every vector's copies
+    must be its lowest-indexed ones, whichever wave's range they sit in (the
+    32 x 32-tile scorer for k <= 16, the 16 x 16 one for k = 17)."""
+    cfg = oenc.Config(seed=5, head_dim=d, bits=bits, qjl=qjl)
+    rng = np.random.default_rng(d + k)
+    base = rng.standard_normal((40, d))
+    ids = rng.permutation(np.repeat(np.arange(40), 300))
+    kb = _oracle_planes(base, cfg)
+    kp = {n: a[ids] for n, a in kb.items()}
+    q = rng.standard_normal((37, d)).astype(np.float32)
+    ref = odec.scores(q.astype(np.float64), kp, cfg)
+    ctx = tq.Context(seed=5, head_dim=d, bits=bits, qjl=qjl)
+    s, i = tq.scores(ctx, torch.from_numpy(q).to(DEV), tq.PackedPlanes.from_numpy(kp), top_k=k)
+    torch.cuda.synchronize()
+    s, i = s.cpu().numpy(), i.cpu().numpy()
+    assert_topk_valid(s, i, ref, k)
+    for qi in range(q.shape[0]):
+        for v in np.unique(ids[i[qi]]):
+            chosen = np.sort(i[qi][ids[i[qi]] == v])
+            lowest = np.sort(np.nonzero(ids == v)[0])[:len(chosen)]
+            assert np.array_equal(chosen, lowest), (qi, v, chosen[:4], lowest[:4])
+    _say("top-k ties: lowest indices chosen", d, bits, qjl, k)
+
+
+@pytest.mark.parametrize("k", [10, 16])
+def test_scores_topk_rising_scores(k):
+    """Keys whose scores rise with the index for every query, so each 32-key
+    step beats every list's threshold: the insertion path at full load."""
+    d = 256
+    cfg = oenc.Config(seed=2, head_dim=d, bits=4, qjl=True)
+    rng = np.random.default_rng(k)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    n = 30000
+    x = np.linspace(0.5, 3.0, n)[:, None] * u[None, :] + 0.01 * rng.standard_normal((n, d))
+    q = (u[None, :] + 0.02 * rng.standard_normal((24, d))).astype(np.float32)
+    kp = _oracle_planes(x, cfg)
+    ref = odec.scores(q.astype(np.float64), kp, cfg)
+    ctx = tq.Context(seed=2, head_dim=d, bits=4, qjl=True)
+    s, i = tq.scores(ctx, torch.from_numpy(q).to(DEV), tq.PackedPlanes.from_numpy(kp), top_k=k)
+    torch.cuda.synchronize()
+    agree = assert_topk_valid(s.cpu().numpy(), i.cpu().numpy(), ref, k)
+    _say("top-k with rising scores: agreement", agree)
+
+
 def test_same_inputs_give_bit_identical_outputs():
     """Run-to-run determinism: encode, decode attention and the fused top-k,
     each called twice on the same inputs, give bit-identical outputs (no
