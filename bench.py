@@ -197,7 +197,7 @@ def search_recall(X, Q, idx, k, n_sample=32):
     import torch
 
     sel = torch.arange(0, Q.shape[0], Q.shape[0] // n_sample)[:n_sample]
-    exact = Q[sel.to(Q.device)].double().cpu() @ X.double().cpu().T
+    exact = Q[sel.to(Q.device)].cpu().double() @ X.cpu().double().T
     top = torch.topk(exact, k, dim=1).indices
     got = idx[sel.to(idx.device)].cpu()
     hits = [len(set(got[r].tolist()) & set(top[r].tolist())) for r in range(len(sel))]

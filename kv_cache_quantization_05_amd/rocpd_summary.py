@@ -6,8 +6,8 @@
 
 --trace: a `rocprofv3 --kernel-trace --stats` run; --fetch / --write: runs of
 `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` over `bench.py
---calibrate-copy`.  The calibrating dispatch is the largest copy kernel of
-the run, which moves exactly 1 GiB; each counter is scaled by
+--calibrate-copy`.  The calibrating dispatch is the largest runtime buffer
+copy (copyBuffer) of the run, which moves exactly 1 GiB; each counter is scaled by
 1 GiB / (its reading for that dispatch), so the reported bytes are in the
 units of a plain copy of known size.  Databases are deleted after reading
 (they are large); the text keeps the figures used.
@@ -38,12 +38,12 @@ GROUPS = {
     "attend_decode": re.compile(r"attend_mfma_kernel|attend_partial_kernel|attend_merge_kernel|query_prep_kernel"),
     "attend_prefill": re.compile(r"prefill_kernel|rotate_back_kernel"),
     "encode": re.compile(r"encode_kernel|encode_qjl_kernel|encode_qjl_mfma_kernel|encode_mfma_kernel|encode_var_kernel|encode_haar_kernel"),
-    "scores": re.compile(r"scores_mfma_kernel|scores_topk_kernel|scores_full_kernel|topk_merge_kernel"),
+    "scores": re.compile(r"scores_tile32_kernel|scores_mfma_kernel|scores_topk_kernel|scores_full_kernel|topk_merge_kernel"),
 }
 # dispatches that count launches of each group
 ANCHORS = {"attend_decode": re.compile(r"attend_merge_kernel"), "encode": GROUPS["encode"],
            "attend_prefill": re.compile(r"prefill_kernel"),
-           "scores": re.compile(r"scores_mfma_kernel|scores_topk_kernel|scores_full_kernel")}
+           "scores": re.compile(r"scores_tile32_kernel|scores_mfma_kernel|scores_topk_kernel|scores_full_kernel")}
 QUERY = re.compile(r"query_prep_kernel")
 DECODE_ONLY = re.compile(r"attend_mfma_kernel|attend_partial_kernel|attend_merge_kernel")
 PREFILL = re.compile(r"prefill_kernel")
@@ -95,7 +95,7 @@ def read_counter(d, counter):
             "where counter_name = ? group by kernel_name", (counter,)))
         copies += [r[0] for r in con.execute(
             "select value from counters_collection where counter_name = ? and "
-            "(kernel_name like '%copyBuffer%' or kernel_name like '%copy_kernel%')", (counter,))]
+            "kernel_name like '%copyBuffer%'", (counter,))]
         con.close()
     return per, copies
 
