@@ -49,8 +49,14 @@ __device__ __forceinline__ int tile_token(int rt, int r) {
     return 32 * (rt >> 1) + 8 * (r >> 2) + 4 * (rt & 1) + (r & 3);
 }
 
+// Two waves per SIMD for MSE-only keys (the query operands and accumulators
+// of two column tiles, plus the prefetched codes, fit 256 registers); QJL
+// keys add S q' operands and run one.
+template <bool QJL>
+constexpr int prefill_waves() { return QJL ? 1 : 2; }
+
 template <int D, int KB, int VB, bool QJL, int NCT, int NW>
-__global__ __launch_bounds__(64 * NW) void prefill_kernel(const dev_tables kt, const dev_tables vt, const prefill_args a) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(prefill_waves<QJL>()))) void prefill_kernel(const dev_tables kt, const dev_tables vt, const prefill_args a) {
     constexpr int KS = D / 32;          // k-steps of the logits
     constexpr int DT = D / 16;          // 16-dim tiles of the output
     constexpr int KRS = D + 8;          // key rows in LDS (halves): rows 16 B apart in the banks
@@ -129,54 +135,77 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const dev_tables kt, c
     const int64_t kvb = int64_t(b) * a.k.stride[0] + int64_t(g) * a.k.stride[1];
     const int64_t vvb = int64_t(b) * a.v.stride[0] + int64_t(g) * a.v.stride[1];
 
+    // The next tile's codes, signs and norms are loaded into registers while
+    // the current tile is processed (each thread decodes the same units of
+    // every tile: unit u = (token u % kPT, block u / kPT), u = tid + 256 i).
+    constexpr int kUnits = kPT * KS;
+    constexpr int UPT = (kUnits + 255) / 256;
+    uint32_t kwn[UPT][KB], vwn[UPT][VB], ksn[UPT];
+    uint16_t knn[UPT], krn[UPT], vnn[UPT];
+    auto load_tile = [&](int64_t t0) {
+#pragma unroll
+        for (int i = 0; i < UPT; ++i) {
+            const int u = tid + 256 * i;
+            if (u >= kUnits) break;
+            const int tt = u % kPT, bl = u / kPT;
+            const int64_t t = t0 + tt;
+            const bool ok = t < kend;
+            const int64_t kv = kvb + (ok ? t : 0) * a.k.stride[2];
+            const int64_t vv = vvb + (ok ? t : 0) * a.v.stride[2];
+            const uint32_t * kc = reinterpret_cast<const uint32_t *>(a.k.codes + kv * (D * KB / 8)) + bl * KB;
+            const uint32_t * vc = reinterpret_cast<const uint32_t *>(a.v.codes + vv * (D * VB / 8)) + bl * VB;
+#pragma unroll
+            for (int k = 0; k < KB; ++k) kwn[i][k] = ok ? kc[k] : 0u;
+#pragma unroll
+            for (int k = 0; k < VB; ++k) vwn[i][k] = ok ? vc[k] : 0u;
+            if constexpr (QJL) ksn[i] = ok ? reinterpret_cast<const uint32_t *>(a.k.signs + kv * (D / 8))[bl] : 0u;
+            if (bl == 0) {
+                knn[i] = ok ? a.k.norms[kv] : uint16_t(0);
+                vnn[i] = ok ? a.v.norms[vv] : uint16_t(0);
+                if constexpr (QJL) krn[i] = ok ? a.k.rnorms[kv] : uint16_t(0);
+            }
+        }
+    };
+    if (kend > 0) load_tile(0);
+
     for (int64_t t0 = 0; t0 < kend; t0 += kPT) {
         __syncthreads();   // the previous tile's LDS reads are done
         // ---- dequantise the tile: unit (token, 32-code block), a wave's 64
         // lanes taking one block of the tile's 64 tokens, so the transposed
         // value stores of one instruction fill consecutive halves of one row
-        // (with 8 waves, waves 0-3 decode the keys and waves 4-7 the values)
-        const bool do_k = NW == 4 || tid < 256, do_v = NW == 4 || tid >= 256;
-        for (int u = tid & 255; u < kPT * KS; u += 256) {
-            const int tt = u % kPT, bl = u / kPT;
-            const int64_t t = t0 + tt;
-            const bool ok = t < kend;
-            if (do_k) {
-                const int64_t kv = kvb + t * a.k.stride[2];
-                const uint32_t * kc = reinterpret_cast<const uint32_t *>(a.k.codes + kv * (D * KB / 8)) + bl * KB;
-                uint32_t kw[KB];
 #pragma unroll
-                for (int k = 0; k < KB; ++k) kw[k] = ok ? kc[k] : 0u;
+        for (int i = 0; i < UPT; ++i) {
+            const int u = tid + 256 * i;
+            if (u >= kUnits) break;
+            const int tt = u % kPT, bl = u / kPT;
+            const bool ok = t0 + tt < kend;
+            {
                 uint32_t kp[16];
 #pragma unroll
                 for (int q4 = 0; q4 < 8; ++q4) {
                     uint32_t sel = 0;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) sel |= block_code<KB>(kw, 4 * q4 + j) << (8 * j);
+                    for (int j = 0; j < 4; ++j) sel |= block_code<KB>(kwn[i], 4 * q4 + j) << (8 * j);
                     lut4<KB>(klut, sel, kp[2 * q4], kp[2 * q4 + 1]);
                 }
                 uint4 * kd = reinterpret_cast<uint4 *>(&klds[tt * KRS + 32 * bl]);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) kd[c] = uint4{kp[4 * c], kp[4 * c + 1], kp[4 * c + 2], kp[4 * c + 3]};
-                if constexpr (QJL) ksl[tt][bl] = ok ? reinterpret_cast<const uint32_t *>(a.k.signs + kv * (D / 8))[bl] : 0u;
+                if constexpr (QJL) ksl[tt][bl] = ksn[i];
                 if (bl == 0) {
                     // per-token factors: the key norm with the logit scale (base
                     // 2) and 1/sqrt(d); the QJL term's gamma sqrt(pi/2)/m on top
-                    const float nk = ok ? half_bits_to_float(a.k.norms[kv]) * s2scale : 0.f;
+                    const float nk = ok ? half_bits_to_float(knn[i]) * s2scale : 0.f;
                     knl[tt] = nk * inv_sqrt_d;
-                    if constexpr (QJL) krl[tt] = ok ? half_bits_to_float(a.k.rnorms[kv]) * qjl_coef * nk : 0.f;
+                    if constexpr (QJL) krl[tt] = ok ? half_bits_to_float(krn[i]) * qjl_coef * nk : 0.f;
                 }
             }
-            if (do_v) {
-                const int64_t vv = vvb + t * a.v.stride[2];
-                const uint32_t * vc = reinterpret_cast<const uint32_t *>(a.v.codes + vv * (D * VB / 8)) + bl * VB;
-                uint32_t vw[VB];
-#pragma unroll
-                for (int k = 0; k < VB; ++k) vw[k] = ok ? vc[k] : 0u;
+            {
 #pragma unroll
                 for (int q4 = 0; q4 < 8; ++q4) {
                     uint32_t vsel = 0;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) vsel |= block_code<VB>(vw, 4 * q4 + j) << (8 * j);
+                    for (int j = 0; j < 4; ++j) vsel |= block_code<VB>(vwn[i], 4 * q4 + j) << (8 * j);
                     uint32_t v0, v1;
                     lut4<VB>(vlut, vsel, v0, v1);
                     const int dim0 = 32 * bl + 4 * q4;
@@ -185,9 +214,10 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(const dev_tables kt, c
                     vlds[(dim0 + 2) * VRS + tt] = static_cast<uint16_t>(v1);
                     vlds[(dim0 + 3) * VRS + tt] = static_cast<uint16_t>(v1 >> 16);
                 }
-                if (bl == 0) vnl[tt] = ok ? half_bits_to_float(a.v.norms[vv]) * inv_sqrt_d : 0.f;
+                if (bl == 0) vnl[tt] = ok ? half_bits_to_float(vnn[i]) * inv_sqrt_d : 0.f;
             }
         }
+        if (t0 + kPT < kend) load_tile(t0 + kPT);
         __syncthreads();
         // the running largest value weight scale (weights stay in [0, 1] in
         // fp16); the same in every wave of the workgroup
