@@ -275,12 +275,14 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(const scores_args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core scorer, d = 128 or 256.  The score matrix of 16 queries x 16
-// keys is a real dense contraction: v_mfma_f32_16x16x32_f16 with the queries
-// as the A operand (held in registers for the whole key range: R q as fp16
-// hi + lo, ~22 bits, and S R q as fp16, whose contribution is scaled by
-// gamma sqrt(pi/2)/m and needs no more) and the keys as the B operand (fp16
-// centroids and +-1 signs, exact, unpacked with byte permutes).  Lane group g
+// Matrix-core scorer on 16 x 16 tiles, d = 128 or 256, for top-k lists
+// longer than the 32 x 32-tile scorer keeps (16 < k <= 64).  The score
+// matrix of 16 queries x 16 keys is a real dense contraction:
+// v_mfma_f32_16x16x32_f16 with the queries as the A operand (held in
+// registers for the whole key range: R q as fp16 hi + lo, ~22 bits, and
+// S R q as fp16, whose contribution is scaled by gamma sqrt(pi/2)/m and needs
+// no more) and the keys as the B operand (fp16 centroids and +-1 signs,
+// exact, unpacked with byte permutes).  Lane group g
 // (lanes 16g..16g+15) unpacks blocks d/128 g .. of its key, so a lane's key
 // is also the key of its output column: norms and gamma stay in the lane.
 // Top-k keeps a sorted list per query in LDS, touched only by scores that

@@ -407,6 +407,7 @@ void scores_tile32_kernel(const dev_tables t, const scores_args a) {
             }
             // queries 4 w .. 4 w + 3: the smallest c-th best over the eight
             // waves (lane 4 w' + r reads wave w' of query 4 w + r)
+            static_assert(kWaves == 8, "32 lanes cover 4 queries x 8 waves");
             if (lane < 32) {
                 const int m = 4 * wave + (lane & 3);
                 float c = pub[lane >> 2][m];
