@@ -16,7 +16,7 @@ What the pages fix:
   * Quantisation uses a table of centroids ([TQ+ guide] §5.2, Phase-1 file
     list; §5.3 names an fp16 centroid LUT).
 
-Readings taken where the pages are silent (listed in the design doc as well):
+Readings taken where the pages are silent:
   * PRNG: SplitMix64 (Steele, Lea and Flood, OOPSLA 2014).  D1 is the first d
     outputs of a generator seeded with `seed`, D2 the next d outputs; an
     output gives +1 when its top bit is 0, else -1.
