@@ -508,6 +508,32 @@ def test_scores_topk_rising_scores(k):
     _say("top-k with rising scores: agreement", agree)
 
 
+@pytest.mark.parametrize("d,bits,qjl", [(256, 4, True), (128, 3, False)])
+@pytest.mark.parametrize("n_k,n_q", [(1, 1), (7, 3), (31, 33), (33, 1), (95, 64)])
+def test_scores_tiny_key_sets(d, bits, qjl, n_k, n_q):
+    """Key sets shorter than one 32-key step or a few steps long, and one or
+    a few queries: most waves of the workgroup have no key range, the first
+    step is partly past the end; full matrix and top-k (k up to n_k)."""
+    cfg = oenc.Config(seed=4, head_dim=d, bits=bits, qjl=qjl)
+    rng = np.random.default_rng(n_k * 131 + n_q + d)
+    x = rng.standard_normal((n_k, d))
+    q = rng.standard_normal((n_q, d)).astype(np.float32)
+    kp = _oracle_planes(x, cfg)
+    # attention-logit scale (N(0,1) vectors: logits of order 1)
+    scale = 1 / math.sqrt(d)
+    ref = odec.scores(q.astype(np.float64), kp, cfg, scale=scale)
+    ctx = tq.Context(seed=4, head_dim=d, bits=bits, qjl=qjl)
+    planes = tq.PackedPlanes.from_numpy(kp)
+    full = tq.scores(ctx, torch.from_numpy(q).to(DEV), planes, top_k=0, scale=scale)
+    torch.cuda.synchronize()
+    assert np.abs(full.cpu().numpy() - ref).max() <= LOGIT_ATOL
+    for k in sorted({1, min(10, n_k), min(16, n_k)}):
+        s, i = tq.scores(ctx, torch.from_numpy(q).to(DEV), planes, top_k=k, scale=scale)
+        torch.cuda.synchronize()
+        assert_topk_valid(s.cpu().numpy(), i.cpu().numpy(), ref, k)
+    _say("tiny key sets", d, bits, qjl, n_k, n_q)
+
+
 def test_same_inputs_give_bit_identical_outputs():
     """Run-to-run determinism: encode, decode attention and the fused top-k,
     each called twice on the same inputs, give bit-identical outputs (no
