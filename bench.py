@@ -25,6 +25,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+
+
+def spread(ms):
+    """Median and (p10, p90) of a list of per-step times."""
+    v = sorted(ms)
+    return v[len(v) // 2], (v[len(v) // 10], v[(9 * len(v)) // 10])
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -156,7 +162,9 @@ def bench_search(args, w):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     enc_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs)
-    sc_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / len(evs)
+    sc_list = [e[1].elapsed_time(e[2]) for e in evs]
+    sc_ms = sum(sc_list) / len(sc_list)
+    sc_med, sc_pp = spread(sc_list)
     flops = float(nq) * n * (2 * w.d + (2 * kctx.sign_bytes * 8 if w.k_qjl else 0))
     tflops = flops / (sc_ms * 1e-3) / 1e12
     enc_bytes = X.numel() * X.element_size() + packed
@@ -170,6 +178,8 @@ def bench_search(args, w):
         "config": {"workload": w.name, "n": n, "n_queries": nq, "head_dim": w.d, "bits": w.k_bits,
                    "qjl": w.k_qjl, "top_k": k_top, "packed_bytes": int(packed)},
         "scores_ms": round(sc_ms, 4),
+        "scores_ms_median": round(sc_med, 4),
+        "scores_ms_p10_p90": [round(sc_pp[0], 4), round(sc_pp[1], 4)],
         "encode_us": round(enc_ms * 1e3, 2),
         "encode_mtok_s": round(n / (enc_ms * 1e-3) / 1e6, 2),
         # the scorer is an fp16 matrix-core contraction (algorithmic flops:
@@ -288,7 +298,9 @@ def bench_prefill(args, w):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     enc_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs)
-    pf_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / len(evs)
+    pf_list = [e[1].elapsed_time(e[2]) for e in evs]
+    pf_ms = sum(pf_list) / len(pf_list)
+    pf_med, pf_pp = spread(pf_list)
     pairs = sum(min(i + 1 + (w.T - Tq), w.T) for i in range(Tq))   # visible keys over the block
     flops = float(w.B) * w.Hq * pairs * 4 * w.d
     tflops = flops / (pf_ms * 1e-3) / 1e12
@@ -304,6 +316,8 @@ def bench_prefill(args, w):
                    "k_bits": w.k_bits, "v_bits": w.v_bits, "k_qjl": w.k_qjl, "input": w.in_dtype,
                    "packed_bytes": int(packed)},
         "prefill_us": round(pf_ms * 1e3, 2),
+        "prefill_us_median": round(pf_med * 1e3, 2),
+        "prefill_us_p10_p90": [round(pf_pp[0] * 1e3, 2), round(pf_pp[1] * 1e3, 2)],
         "encode_us": round(enc_ms * 1e3, 2),
         "encode_mtok_s": round(w.B * w.T / (enc_ms * 1e-3) / 1e6, 2),
         "roofline": {"kernel": "attend_prefill", "bound": "mfma", "achieved": round(tflops, 3), "peak": 2500.0,
@@ -322,7 +336,7 @@ def bench_prefill(args, w):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama_b4_t128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -435,7 +449,8 @@ def main():
                    "packed_bytes": int(packed), "rotation_copies": [R_in, R_pk]},
         "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
         "decode_us": round(dec_avg * 1e3, 2),
-        "decode_us_p10_p90": [round(dec_ms[len(dec_ms) // 10] * 1e3, 2), round(dec_ms[(9 * len(dec_ms)) // 10] * 1e3, 2)],
+        "decode_us_median": round(spread(dec_ms)[0] * 1e3, 2),
+        "decode_us_p10_p90": [round(spread(dec_ms)[1][0] * 1e3, 2), round(spread(dec_ms)[1][1] * 1e3, 2)],
         "encode_us": round(enc_avg * 1e3, 2),
         "encode_mtok_s": round(enc_mtoks, 2),
         "roofline": r_dec,
