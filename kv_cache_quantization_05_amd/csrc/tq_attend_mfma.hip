@@ -465,9 +465,36 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     // (block gs % 16 of k-step gs holds head lane & 3 at dims of k-step gs).
     // fp16 suffices: the sketch term is a small correction weighted by the
     // residual norm, so 2^-11 relative error in S q' stays far below the
-    // logit tolerance.
+    // logit tolerance.  The signs enter as b in {0, 1} (expand_signs): the A
+    // value of bit position k' carries 2^(24 - k' - E), E from the block's
+    // largest |S q'| (every A value a normal fp16 below 2^15), and each head's
+    // accumulator starts at -sum(S q') 2^-(E+1); scaled by 2^(E+1) it is
+    // sum (S q')_i sigma_i.
     half4 au[2];
+    floatx4 sq0 = {0.f, 0.f, 0.f, 0.f};
+    int qe = 0;
     if constexpr (QJL) {
+        // the same figures in every wave: lane l reads S q' entries l + 64 j
+        // of the four heads (max), and 8 entries of head l / 16 (sum)
+        float mu = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int f = lane + 64 * j;
+            mu = fmaxf(mu, fabsf(qsrc[(f >> 7) * qstride + kD + (f & 127)]));
+        }
+        int ex;
+        frexpf(wave_max_uniform(mu), &ex);  // the largest |S q'| < 2^ex
+        qe = ex + 9;
+        float su = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) su += qsrc[(lane >> 4) * qstride + kD + 8 * (lane & 15) + j];
+        su += lane_xor<1>(su);
+        su += lane_xor<2>(su);
+        su += lane_xor<4>(su);
+        su += lane_xor<8>(su);
+#pragma unroll
+        for (int h = 0; h < kG; ++h)
+            sq0[h] = ldexpf(-__int_as_float(__builtin_amdgcn_readlane(__float_as_int(su), 16 * h)), -(qe + 1));
         const float * qrow = qsrc + (lane & 3) * qstride;
 #pragma unroll
         for (int set = 0; set < 2; ++set) {
@@ -475,7 +502,8 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
             const int bl = gs >> 3, kk = gs & 7;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                au[set][i] = static_cast<_Float16>(qrow[kD + 32 * bl + sign_bit_of_pos(4 * kk + i)]);
+                au[set][i] = static_cast<_Float16>(
+                    ldexpf(qrow[kD + 32 * bl + sign_bit_of_pos(4 * kk + i)], 24 - sign_shift_of_pos(4 * kk + i) - qe));
         }
     }
     const uint32_t lane_off = uint32_t(lane & 31) * 4;  // pair-table copy of this lane
@@ -483,7 +511,7 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
     // logits are kept in base-2 units (scaled by log2 e), so weights are plain
     // exp2; the reference is converted back to natural units at the end
     const float kscale = a.scale * (BN ? 1.0f / sqrtf(32.f) : inv_sqrt_d) * float(M_LOG2E);
-    const float qjl_gain = sqrtf(0.5f * float(M_PI)) / float(kD) * sqrtf(float(kD));
+    const float qjl_gain = ldexpf(sqrtf(0.5f * float(M_PI)) / float(kD) * sqrtf(float(kD)), qe + 1);
     const float w_cap = __expf(kSlack);
 
     // acc[gd]: heads x dim (32 blk + 4 gd + (lane & 3)), blk = (lane >> 2) & 3,
@@ -571,11 +599,11 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
             }
         }
         if constexpr (QJL) {
-            floatx4 Sq[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            floatx4 Sq[2] = {sq0, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int bl = 0; bl < 4; ++bl) {
                 uint32_t bs[16];
-                unpack_signs(r.ks[bl], bs);
+                expand_signs(r.ks[bl], bs);
 #pragma unroll
                 for (int kk = 0; kk < 8; ++kk) {
                     const int gs = 8 * bl + kk;

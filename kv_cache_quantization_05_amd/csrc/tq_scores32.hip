@@ -63,17 +63,6 @@ __device__ __forceinline__ half8 as_half8(const uint32_t * w) {
     return h;
 }
 
-// 32 sign bits -> 16 dwords of fp16 pairs: pair k = (bit k, bit k + 16) as
-// b 2^(k' - 24), k' = k for k < 10 and k - 6 above (exact fp16 denormals).
-__device__ __forceinline__ void expand_signs(uint32_t bits, uint32_t * out) {
-    const uint32_t b6 = bits >> 6;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) out[k] = k < 10 ? (bits & (0x00010001u << k)) : (b6 & (0x00010001u << (k - 6)));
-}
-
-// Position k' of the sign bit behind fp16 half `pos` of expand_signs' output.
-__host__ __device__ constexpr int sign_shift_of_pos(int pos) { return (pos >> 1) < 10 ? (pos >> 1) : (pos >> 1) - 6; }
-
 // (score desc, index asc) ordering
 __device__ __forceinline__ bool ahead_of(float s1, int32_t i1, float s2, int32_t i2) {
     return s1 > s2 || (s1 == s2 && i1 < i2);

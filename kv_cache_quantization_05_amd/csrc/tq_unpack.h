@@ -146,6 +146,21 @@ __device__ __forceinline__ void unpack_signs(uint32_t bits, uint32_t * out) {
 // Bit index inside the 32-bit sign word of output half `pos`.
 __host__ __device__ constexpr int sign_bit_of_pos(int pos) { return (pos >> 1) + 16 * (pos & 1); }
 
+// 32 sign bits -> 16 dwords of fp16 pairs in the same order, as b in {0, 1}
+// instead of +-1: pair k = (bit k, bit k + 16) as b 2^(k' - 24), k' = k for
+// k < 10 and k - 6 above (exact fp16 denormals, one AND each: the bits stay
+// in place).  A product against them uses sigma = 2 b - 1: the other operand
+// carries 2^(24 - k') times a common power of two, and the sum of that operand
+// is subtracted.
+__device__ __forceinline__ void expand_signs(uint32_t bits, uint32_t * out) {
+    const uint32_t b6 = bits >> 6;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) out[k] = k < 10 ? (bits & (0x00010001u << k)) : (b6 & (0x00010001u << (k - 6)));
+}
+
+// Position k' of the sign bit behind fp16 half `pos` of expand_signs' output.
+__host__ __device__ constexpr int sign_shift_of_pos(int pos) { return (pos >> 1) < 10 ? (pos >> 1) : (pos >> 1) - 6; }
+
 // 3- and 4-bit codes can instead be decoded through an LDS
 // table indexed by two consecutive codes (2 BITS bits of the row's bit
 // stream): entry e holds the fp16 centroids of codes e & (2^BITS - 1) and
