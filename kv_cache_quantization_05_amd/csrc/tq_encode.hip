@@ -177,10 +177,14 @@ __global__ __launch_bounds__(256) void encode_kernel(const dev_tables t, const e
 // the sign bits of h ([Orión plan] Fase 3; [TQ explainer] §2.2).  The sign
 // of S rho equals the sign of S r, rho = r / sqrt(d).
 template <int D, int BITS, bool BF16>
-__global__ __launch_bounds__(256) void encode_qjl_kernel(const dev_tables t, const encode_args a,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void encode_qjl_kernel(const dev_tables t, const encode_args a,
                                                          const grid_index gi, const uint32_t nvec) {
     constexpr int LPV = D / 32;
-    constexpr int VPB = 256 / LPV;   // vectors per workgroup iteration
+    // vectors per workgroup iteration: NR rounds of phase A (256 / LPV
+    // vectors each), so that every S fragment a k-step loads feeds at least
+    // four 16-vector column tiles of phase B
+    constexpr int NR = D == 256 ? 2 : 1;
+    constexpr int VPB = NR * 256 / LPV;
     constexpr uint32_t kHalf = 1u << (BITS - 1);
     constexpr int RS = D + 8;        // LDS row stride (halves): rows start 16 B apart in the banks
     constexpr int RT = D / 16;       // 16-row tiles of S (m = d)
@@ -192,7 +196,6 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(const dev_tables t, con
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int blk = tid % LPV;
-    const int vl = tid / LPV;        // vector within the workgroup's batch
     const uint32_t d1w = t.d1[blk];
     const uint32_t d2w = t.d2[blk];
     // positive thresholds th[2^(b-1) + j]; the codebook is exactly symmetric
@@ -205,6 +208,9 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(const dev_tables t, con
     const uint16_t * const s_lo = t.S16 + D * D;
 
     for (uint32_t base = blockIdx.x * VPB; base < nvec; base += gridDim.x * VPB) {
+#pragma unroll 1
+      for (int rd = 0; rd < NR; ++rd) {
+        const int vl = tid / LPV + rd * (256 / LPV);   // vector within the workgroup's batch
         const uint32_t v = base + vl;
         const bool valid = v < nvec;
         int64_t xoff, pv;
@@ -281,6 +287,7 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(const dev_tables t, con
                 dl[q] = uint4{rlo[4 * q], rlo[4 * q + 1], rlo[4 * q + 2], rlo[4 * q + 3]};
             }
         }
+      }
         __syncthreads();
 
         // ---------------- phase B: rows 16 rt .. +15 of h for 16 vectors per
