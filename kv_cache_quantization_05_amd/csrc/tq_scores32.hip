@@ -38,10 +38,11 @@
 // fill the lists by one sort per half-wave.  Afterwards a score enters only
 // if it reaches the workgroup's threshold for its query, a value that at
 // least k distinct keys already reach: the largest k-th best of the eight
-// waves' lists, raised to the smallest c-th best over the lists (c =
-// ceil(k / waves), so at least k keys).  The k-th best of all keys is at least
-// that value, so no key of the final top-k is ever filtered out, and none is
-// evicted from its list (fewer than k keys beat it).
+// waves' lists, raised to the j-th largest of the lists' c-th bests (c =
+// ceil(k / waves), j = ceil(k / c): j lists hold c keys each at or above it,
+// j c >= k distinct keys).  The k-th best of all keys is at least that value,
+// so no key of the final top-k is ever filtered out, and none is evicted from
+// its list (fewer than k keys beat it).
 #include <cmath>
 
 #include "tq_device.h"
@@ -70,6 +71,18 @@ __device__ __forceinline__ bool ahead_of(float s1, int32_t i1, float s2, int32_t
 
 // Lane l - 1's value within each row of 16 lanes (lane 0 of a row: x).
 __device__ __forceinline__ int32_t row_shr1(int32_t x) { return __builtin_amdgcn_update_dpp(x, x, 0x111, 0xF, 0xF, false); }
+
+// Eight values in registers sorted largest first (a 19-comparator network).
+__device__ __forceinline__ void sort8_desc(float * e) {
+    constexpr int net[19][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}, {0, 4}, {1, 5}, {2, 6}, {3, 7}, {0, 1}, {2, 3},
+                                {4, 5}, {6, 7}, {2, 4}, {3, 5}, {1, 4}, {3, 6}, {1, 2}, {3, 4}, {5, 6}};
+#pragma unroll
+    for (int c = 0; c < 19; ++c) {
+        const float a = e[net[c][0]], b = e[net[c][1]];
+        e[net[c][0]] = fmaxf(a, b);
+        e[net[c][1]] = fminf(a, b);
+    }
+}
 
 // Bitonic sort of (s, i) within each 32-lane half of the wave, best first.
 __device__ __forceinline__ void half_sort32(float & s, int32_t & i, int lane) {
@@ -106,7 +119,7 @@ void scores_tile32_kernel(const dev_tables t, const scores_args a) {
     // thr[h][4 i + j] belongs to query 8 i + 4 h + j
     __shared__ __align__(16) float thr[2][16];
     // each wave's c-th best per query
-    __shared__ float pub[kWaves][32];
+    __shared__ __align__(16) float pub[32][kWaves];
     __shared__ float sum_u[32];
     __shared__ float max_u;
     uint8_t * const frag_lo = lds_all;
@@ -205,14 +218,16 @@ void scores_tile32_kernel(const dev_tables t, const scores_args a) {
             for (int e = 0; e < 8; ++e) aqh[s][e] = static_cast<_Float16>(qrow[dim_of(lane, s, e)]);
     }
     const int K = a.top_k;
-    // c: (waves with a range) * c >= K; a wave without a range takes no part
-    // in the smallest c-th best (its entry stays +inf)
+    // c: (waves with a range) * c >= K, and jc = ceil(K / c) <= waves with a
+    // range; a wave without a range holds -inf entries, below every jc-th
+    // largest
     const int active = static_cast<int>(a.n_ranges - (item / n_qt) * kWaves < kWaves ? a.n_ranges - (item / n_qt) * kWaves
                                                                                   : kWaves);
     const int kc = (K + active - 1) / active;
+    const int jc = (K + kc - 1) / kc;
     if constexpr (TOPK) {
         if (tid < 32) thr[tid >> 4][tid & 15] = -INFINITY;
-        if (lane < 32) pub[wave][lane] = has_range ? -INFINITY : INFINITY;
+        if (lane < 32) pub[lane][wave] = -INFINITY;
     }
     __syncthreads();
 
@@ -333,7 +348,7 @@ void scores_tile32_kernel(const dev_tables t, const scores_args a) {
                     li[v] = iv;
                 }
                 if (n32 == K - 1) __hip_atomic_fetch_max(&thr[h][v], sv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                if (n32 == kc - 1) pub[wave][m] = sv;
+                if (n32 == kc - 1) pub[m][wave] = sv;
             }
             __builtin_amdgcn_wave_barrier();
         } else {
@@ -390,22 +405,24 @@ void scores_tile32_kernel(const dev_tables t, const scores_args a) {
                         const int m = 8 * (v >> 2) + 4 * lane + (v & 3);
                         __hip_atomic_fetch_max(&thr[lane][v], lane ? kth1 : kth0, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_WORKGROUP);
-                        pub[wave][m] = lane ? cth1 : cth0;
+                        pub[m][wave] = lane ? cth1 : cth0;
                     }
                 }
             }
-            // queries 4 w .. 4 w + 3: the smallest c-th best over the eight
-            // waves (lane 4 w' + r reads wave w' of query 4 w + r)
-            static_assert(kWaves == 8, "32 lanes cover 4 queries x 8 waves");
-            if (lane < 32) {
-                const int m = 4 * wave + (lane & 3);
-                float c = pub[lane >> 2][m];
-                c = fminf(c, __shfl_xor(c, 4));
-                c = fminf(c, __shfl_xor(c, 8));
-                c = fminf(c, __shfl_xor(c, 16));
-                if (lane < 4)
-                    __hip_atomic_fetch_max(&thr[(m >> 2) & 1][4 * (m >> 3) + (m & 3)], c, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+            // every fourth step, queries 4 w .. 4 w + 3 (lane r: query 4 w + r):
+            // the jc-th largest of the eight waves' c-th bests
+            static_assert(kWaves == 8, "a sorting network of the eight waves' entries");
+            if ((((j0 - k_begin) >> 5) & 3) == 0 && lane < 4) {
+                const int m = 4 * wave + lane;
+                const float4 x0 = *reinterpret_cast<const float4 *>(&pub[m][0]);
+                const float4 x1 = *reinterpret_cast<const float4 *>(&pub[m][4]);
+                float e[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                sort8_desc(e);
+                float c = e[0];
+#pragma unroll
+                for (int i = 1; i < 8; ++i) c = jc - 1 == i ? e[i] : c;
+                __hip_atomic_fetch_max(&thr[(m >> 2) & 1][4 * (m >> 3) + (m & 3)], c, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         }
     }
