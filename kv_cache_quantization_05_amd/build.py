@@ -2,8 +2,9 @@
 
     python -m kv_cache_quantization_05_amd.build [--jobs N]
 
-Every translation unit under csrc/ is compiled to an object file, then all
-are linked into kv_cache_quantization_05_amd/libtq.so.  Packed-FP32 VALU
+Every translation unit under csrc/ is compiled to an object file (the
+general decode kernels, tq_attend_dims.hip, once per head dimension), then
+all are linked into kv_cache_quantization_05_amd/libtq.so.  Packed-FP32 VALU
 instructions are disabled for device code (-packed-fp32-ops).
 """
 
@@ -35,13 +36,29 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
+HEAD_DIMS = (32, 64, 128, 256)
+PER_DIM = "tq_attend_dims.hip"  # compiled once per head dimension
+
+
 def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + COMMON
+def units():
+    """(source, extra flags, object name) of every compile job."""
+    out = []
+    for src in sources():
+        if src == PER_DIM:
+            out += [(src, [f"-DTQ_HEAD_DIM={d}"], f"{src}.d{d}.o") for d in HEAD_DIMS]
+        else:
+            out.append((src, [], src + ".o"))
+    return out
+
+
+def _compile(unit):
+    src, extra, name = unit
+    obj = os.path.join(BUILD, name)
+    cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + COMMON + extra
     if src.endswith(".hip"):
         cmd += DEVICE
     else:
@@ -54,7 +71,9 @@ def _compile(src):
 
 def build(jobs=8, verbose=True):
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
+    srcs = units()
+    # the slowest units first, so that they do not start last
+    srcs.sort(key=lambda u: u[0] != PER_DIM)
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = OUT + ".tmp"
@@ -64,7 +83,7 @@ def build(jobs=8, verbose=True):
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, OUT)
     if verbose:
-        print(f"built {OUT} from {len(srcs)} sources")
+        print(f"built {OUT} from {len(sources())} sources ({len(srcs)} objects)")
     return OUT
 
 

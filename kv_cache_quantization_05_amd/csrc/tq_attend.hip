@@ -1,18 +1,25 @@
 // Decode attention dispatch: query prep, partial kernels, merge.
 #include <atomic>
 
+#include "tq_attend_v1.h"
 #include "tq_internal.h"
 
 namespace tq {
 
-#define TQ_DECLARE_DIM(D)                                                                              \
-    hipError_t launch_attend_dim##D(const dev_tables &, const dev_tables &, const attend_args &, hipStream_t); \
-    hipError_t launch_prep_dim##D(const dev_tables &, const float *, int64_t, float *, int64_t, hipStream_t);
-TQ_DECLARE_DIM(32)
-TQ_DECLARE_DIM(64)
-TQ_DECLARE_DIM(128)
-TQ_DECLARE_DIM(256)
-#undef TQ_DECLARE_DIM
+// The general launchers are instantiated in tq_attend_dims.hip, one object
+// file per head dimension.
+namespace v1 {
+#define TQ_EXTERN_DIM(D)                                                                                  \
+    extern template hipError_t launch_attend_d<D>(const dev_tables &, const dev_tables &, const attend_args &, \
+                                                  hipStream_t);                                         \
+    extern template hipError_t launch_prep_d<D>(const dev_tables &, const float *, int64_t, float *, int64_t, \
+                                                hipStream_t);
+TQ_EXTERN_DIM(32)
+TQ_EXTERN_DIM(64)
+TQ_EXTERN_DIM(128)
+TQ_EXTERN_DIM(256)
+#undef TQ_EXTERN_DIM
+}  // namespace v1
 
 // Compute units of the current device, queried once per device.
 int current_cu_count() {
@@ -64,10 +71,10 @@ hipError_t launch_query_prep(const dev_tables & t, const float * q, int64_t n, f
                              int64_t qp_stride, hipStream_t s) {
     if (n == 0) return hipSuccess;
     switch (t.d) {
-        case 32: return launch_prep_dim32(t, q, n, qp, qp_stride, s);
-        case 64: return launch_prep_dim64(t, q, n, qp, qp_stride, s);
-        case 128: return launch_prep_dim128(t, q, n, qp, qp_stride, s);
-        case 256: return launch_prep_dim256(t, q, n, qp, qp_stride, s);
+        case 32: return v1::launch_prep_d<32>(t, q, n, qp, qp_stride, s);
+        case 64: return v1::launch_prep_d<64>(t, q, n, qp, qp_stride, s);
+        case 128: return v1::launch_prep_d<128>(t, q, n, qp, qp_stride, s);
+        case 256: return v1::launch_prep_d<256>(t, q, n, qp, qp_stride, s);
     }
     return hipErrorInvalidValue;
 }
@@ -75,10 +82,10 @@ hipError_t launch_query_prep(const dev_tables & t, const float * q, int64_t n, f
 hipError_t launch_attend(const dev_tables & kt, const dev_tables & vt, const attend_args & a,
                          hipStream_t s) {
     switch (kt.d) {
-        case 32: return launch_attend_dim32(kt, vt, a, s);
-        case 64: return launch_attend_dim64(kt, vt, a, s);
-        case 128: return launch_attend_dim128(kt, vt, a, s);
-        case 256: return launch_attend_dim256(kt, vt, a, s);
+        case 32: return v1::launch_attend_d<32>(kt, vt, a, s);
+        case 64: return v1::launch_attend_d<64>(kt, vt, a, s);
+        case 128: return v1::launch_attend_d<128>(kt, vt, a, s);
+        case 256: return v1::launch_attend_d<256>(kt, vt, a, s);
     }
     return hipErrorInvalidValue;
 }
