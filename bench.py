@@ -53,7 +53,7 @@ def traffic_from_profiles(kernel, workload):
     ent = rec.get(f"{workload}:{kernel}")
     from kv_cache_quantization_05_amd.rocpd_summary import kernel_source_hash
 
-    if not ent or ent.get("source_hash") != kernel_source_hash():
+    if not ent or ent.get("source_hash") != kernel_source_hash(kernel):
         return None
     return ent.get("bytes_per_launch")
 

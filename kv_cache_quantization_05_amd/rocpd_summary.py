@@ -51,12 +51,26 @@ _has_decode = [True]
 _has_prefill = [False]
 
 
-def kernel_source_hash():
-    """Hash of the kernel sources; recorded traffic is valid only for it."""
+# HIP sources whose kernels make up each launch group; every header and host
+# source counts for every group.  Recorded traffic is valid only for the
+# hash of its group's sources.
+GROUP_SOURCES = {
+    "attend_decode": ("tq_attend.hip", "tq_attend_dims.hip", "tq_attend_mfma.hip"),
+    "attend_prefill": ("tq_prefill.hip", "tq_attend.hip", "tq_attend_dims.hip"),
+    "encode": ("tq_encode.hip", "tq_encode_qjl.hip", "tq_encode_var.hip"),
+    "scores": ("tq_scores.hip", "tq_scores32.hip", "tq_attend.hip", "tq_attend_dims.hip"),
+}
+
+
+def kernel_source_hash(group=None):
+    """Hash of the sources a launch group's kernels are built from (every
+    source when group is None)."""
     h = hashlib.sha256()
     csrc = os.path.join(PKG, "csrc")
+    own = GROUP_SOURCES.get(group)
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
+        if f.endswith((".h", ".cpp")) or (f.endswith(".hip") and (own is None or f in own)):
+            h.update(f.encode())
             h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -122,7 +136,8 @@ def main():
     ap.add_argument("--keep-db", action="store_true")
     args = ap.parse_args()
 
-    out = [f"# rocprofv3 summary: workload {args.workload}", f"# kernel sources {kernel_source_hash()}"]
+    out = [f"# rocprofv3 summary: workload {args.workload}",
+           "# kernel sources: " + ", ".join(f"{g} {kernel_source_hash(g)}" for g in GROUP_SOURCES)]
     if args.command:
         out.append(f"# commands: {args.command}")
     trace = read_trace(args.trace)
@@ -188,7 +203,7 @@ def main():
                 rec[f"{args.workload}:{g}"] = {
                     "bytes_per_launch": int(t["FETCH_SIZE"] + t["WRITE_SIZE"]),
                     "fetch_bytes": int(t["FETCH_SIZE"]), "write_bytes": int(t["WRITE_SIZE"]),
-                    "source_hash": kernel_source_hash()}
+                    "source_hash": kernel_source_hash(g)}
         with open(args.traffic_json, "w") as f:
             json.dump(rec, f, indent=1, sort_keys=True)
     if not args.keep_db:
