@@ -86,14 +86,18 @@ def _dbs(d):
 
 
 def read_trace(d):
+    """Per kernel name: name, calls, avg, min, max (us), vgpr, lds, scratch,
+    blocks, median (us)."""
     rows = []
     for db in _dbs(d):
         con = sqlite3.connect(db)
-        rows += list(con.execute(
-            "select name, count(*), avg(duration)/1000.0, min(duration)/1000.0, max(duration)/1000.0, "
-            "max(vgpr_count), max(lds_size), max(scratch_size), "
-            "max(grid_x*grid_y*grid_z/(workgroup_x*workgroup_y*workgroup_z)) "
-            "from kernels group by name order by sum(duration) desc"))
+        for r in con.execute(
+                "select name, count(*), avg(duration)/1000.0, min(duration)/1000.0, max(duration)/1000.0, "
+                "max(vgpr_count), max(lds_size), max(scratch_size), "
+                "max(grid_x*grid_y*grid_z/(workgroup_x*workgroup_y*workgroup_z)) "
+                "from kernels group by name order by sum(duration) desc"):
+            ds = sorted(x[0] / 1000.0 for x in con.execute("select duration from kernels where name = ?", (r[0],)))
+            rows.append(tuple(r) + (ds[len(ds) // 2],))
         con.close()
     return rows
 
@@ -144,19 +148,22 @@ def main():
     _has_decode[0] = any(DECODE_ONLY.search(r[0]) for r in trace)
     _has_prefill[0] = any(PREFILL.search(r[0]) for r in trace)
     out.append("## kernel trace (durations in us)")
-    out.append("kernel | calls | avg_us | min_us | max_us | vgpr | lds | scratch | blocks")
+    out.append("kernel | calls | avg_us | min_us | max_us | vgpr | lds | scratch | blocks | median_us")
     per_group = {}
     for r in trace:
-        out.append(f"{short(r[0])} | {r[1]} | {r[2]:.2f} | {r[3]:.2f} | {r[4]:.2f} | {r[5]} | {r[6]} | {r[7]} | {r[8]}")
+        out.append(f"{short(r[0])} | {r[1]} | {r[2]:.2f} | {r[3]:.2f} | {r[4]:.2f} | {r[5]} | {r[6]} | {r[7]} | {r[8]} | {r[9]:.2f}")
         g = group_of(r[0])
         if g:
-            per_group.setdefault(g, []).append((r[0], r[1], r[2]))
-    out.append("## per launch: total duration of the group's dispatches / launches")
+            per_group.setdefault(g, []).append((r[0], r[1], r[2], r[9]))
+    out.append("## per launch: total duration of the group's dispatches / launches (warm-up launches included);"
+               " median: the sum over the group's kernels of (median duration x dispatches / launches)")
     launches = {}
     for g, ks in per_group.items():
         launches[g] = sum(k[1] for k in ks if ANCHORS[g].search(k[0]))
+        n = max(launches[g], 1)
         total = sum(k[1] * k[2] for k in ks)
-        out.append(f"{g}: {total / max(launches[g], 1):.2f} us per launch over {launches[g]} launches "
+        med = sum(k[1] * k[3] for k in ks)
+        out.append(f"{g}: {total / n:.2f} us per launch (median {med / n:.2f} us) over {launches[g]} launches "
                    f"({', '.join(f'{short(k[0])} x{k[1]}' for k in ks)})")
 
     traffic = {}
