@@ -295,48 +295,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
         // read from LDS feeds all of them
         const int n16 = lane & 15, g4 = lane >> 4;
         constexpr int RW = (RT + 3) / 4;  // row tiles per wave (waves >= RT have none at d = 32)
-        f32x4 acc[RW][CT];
-#pragma unroll
-        for (int rw = 0; rw < RW; ++rw)
-#pragma unroll
-            for (int c = 0; c < CT; ++c) acc[rw][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // one k-step at a time (a full unroll hoists every load and spills)
+        // the row tiles in groups of at most two, so that the accumulators of
+        // a group (two row tiles x CT column tiles) and its S fragments fit
+        // the registers with phase A's state; each group re-reads the
+        // residual tiles from LDS
+        constexpr int RG = RW < 2 ? RW : 2;
 #pragma unroll 1
-        for (int ks = 0; ks < KS; ++ks) {
-            f16x8 ah[RW], al[RW];
+        for (int r0 = 0; r0 < RW; r0 += RG) {
+            f32x4 acc[RG][CT];
 #pragma unroll
-            for (int rw = 0; rw < RW; ++rw) {
-                const int rt = wave + 4 * rw < RT ? wave + 4 * rw : 0;
-                const int64_t so = int64_t(16 * rt + n16) * D + 32 * ks + 8 * g4;
-                ah[rw] = as_f16x8(*reinterpret_cast<const uint4 *>(s_hi + so));
-                al[rw] = as_f16x8(*reinterpret_cast<const uint4 *>(s_lo + so));
-            }
+            for (int rw = 0; rw < RG; ++rw)
 #pragma unroll
-            for (int c = 0; c < CT; ++c) {
-                const int ro = (16 * c + n16) * RS + 32 * ks + 8 * g4;
-                const f16x8 bh = as_f16x8(*reinterpret_cast<const uint4 *>(&rl[0][ro]));
-                const f16x8 bl = as_f16x8(*reinterpret_cast<const uint4 *>(&rl[1][ro]));
+                for (int c = 0; c < CT; ++c) acc[rw][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // one k-step at a time (a full unroll hoists every load and spills)
+#pragma unroll 1
+            for (int ks = 0; ks < KS; ++ks) {
+                f16x8 ah[RG], al[RG];
 #pragma unroll
-                for (int rw = 0; rw < RW; ++rw) {
-                    acc[rw][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rw], bh, acc[rw][c], 0, 0, 0);
-                    acc[rw][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rw], bl, acc[rw][c], 0, 0, 0);
-                    acc[rw][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[rw], bh, acc[rw][c], 0, 0, 0);
+                for (int rw = 0; rw < RG; ++rw) {
+                    const int rt = wave + 4 * (r0 + rw) < RT ? wave + 4 * (r0 + rw) : 0;
+                    const int64_t so = int64_t(16 * rt + n16) * D + 32 * ks + 8 * g4;
+                    ah[rw] = as_f16x8(*reinterpret_cast<const uint4 *>(s_hi + so));
+                    al[rw] = as_f16x8(*reinterpret_cast<const uint4 *>(s_lo + so));
+                }
+#pragma unroll
+                for (int c = 0; c < CT; ++c) {
+                    const int ro = (16 * c + n16) * RS + 32 * ks + 8 * g4;
+                    const f16x8 bh = as_f16x8(*reinterpret_cast<const uint4 *>(&rl[0][ro]));
+                    const f16x8 bl = as_f16x8(*reinterpret_cast<const uint4 *>(&rl[1][ro]));
+#pragma unroll
+                    for (int rw = 0; rw < RG; ++rw) {
+                        acc[rw][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rw], bh, acc[rw][c], 0, 0, 0);
+                        acc[rw][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rw], bl, acc[rw][c], 0, 0, 0);
+                        acc[rw][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[rw], bh, acc[rw][c], 0, 0, 0);
+                    }
                 }
             }
-        }
-        // lane holds rows 16 rt + 4 g4 + i of vector 16 c + n16
+            // lane holds rows 16 rt + 4 g4 + i of vector 16 c + n16
 #pragma unroll
-        for (int c = 0; c < CT; ++c) {
-            const int64_t pvv = pvs[16 * c + n16];
+            for (int c = 0; c < CT; ++c) {
+                const int64_t pvv = pvs[16 * c + n16];
 #pragma unroll
-            for (int rw = 0; rw < RW; ++rw) {
-                uint32_t bits = 0;
+                for (int rw = 0; rw < RG; ++rw) {
+                    uint32_t bits = 0;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) bits |= (acc[rw][c][i] > 0.f ? 1u : 0u) << (4 * g4 + i);
-                bits |= __shfl_xor(bits, 16);
-                bits |= __shfl_xor(bits, 32);
-                if (g4 == 0 && pvv >= 0 && wave + 4 * rw < RT)
-                    reinterpret_cast<uint16_t *>(a.out.signs + pvv * (D / 8))[wave + 4 * rw] = static_cast<uint16_t>(bits);
+                    for (int i = 0; i < 4; ++i) bits |= (acc[rw][c][i] > 0.f ? 1u : 0u) << (4 * g4 + i);
+                    bits |= __shfl_xor(bits, 16);
+                    bits |= __shfl_xor(bits, 32);
+                    const int rt = wave + 4 * (r0 + rw);
+                    if (g4 == 0 && pvv >= 0 && rt < RT)
+                        reinterpret_cast<uint16_t *>(a.out.signs + pvv * (D / 8))[rt] = static_cast<uint16_t>(bits);
+                }
             }
         }
         __syncthreads();  // the residual tile is rewritten by the next iteration
