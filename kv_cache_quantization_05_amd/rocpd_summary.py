@@ -36,17 +36,17 @@ GIB = 1 << 30
 
 GROUPS = {
     "attend_decode": re.compile(r"attend_mfma_kernel|attend_partial_kernel|attend_merge_kernel|query_prep_kernel"),
-    "attend_prefill": re.compile(r"prefill_kernel|rotate_back_kernel"),
+    "attend_prefill": re.compile(r"prefill(32)?_kernel|rotate_back_kernel"),
     "encode": re.compile(r"encode_kernel|encode_qjl_kernel|encode_qjl_mfma_kernel|encode_mfma_kernel|encode_var_kernel|encode_haar_kernel"),
     "scores": re.compile(r"scores_tile32_kernel|scores_mfma_kernel|scores_topk_kernel|scores_full_kernel|topk_merge_kernel"),
 }
 # dispatches that count launches of each group
 ANCHORS = {"attend_decode": re.compile(r"attend_merge_kernel"), "encode": GROUPS["encode"],
-           "attend_prefill": re.compile(r"prefill_kernel"),
+           "attend_prefill": re.compile(r"prefill(32)?_kernel"),
            "scores": re.compile(r"scores_tile32_kernel|scores_mfma_kernel|scores_topk_kernel|scores_full_kernel")}
 QUERY = re.compile(r"query_prep_kernel")
 DECODE_ONLY = re.compile(r"attend_mfma_kernel|attend_partial_kernel|attend_merge_kernel")
-PREFILL = re.compile(r"prefill_kernel")
+PREFILL = re.compile(r"prefill(32)?_kernel")
 _has_decode = [True]
 _has_prefill = [False]
 
