@@ -119,6 +119,51 @@ def cpu_baseline(w, budget_s=12.0):
             "encode_mtok_s": round(enc_mtoks, 6)}
 
 
+def cpu_baseline_prefill(w, budget_s=12.0):
+    """The float64 oracle on the host cores for the prefill workload, on a
+    bounded slice: batch 0, KV head 0 (its Hq/Hkv query heads), a prompt of
+    the first T_s positions (T_s doubled up to about a quarter of the budget):
+    encode, then causal prefill of all T_s positions.  In the line's unit:
+    the slice's packed bytes over its prefill time (the prefill work grows as
+    T_s^2, so the figure is that of the slice, stated with it)."""
+    from kv_cache_quantization_05_amd import workloads as wl
+    from oracle import decode as odec
+    from oracle import encode as oenc
+
+    cores, blas = _cpu_threads()
+    G = w.Hq // w.Hkv
+    kc = oenc.Config(**wl.context_kwargs(w, "k"))
+    vc = oenc.Config(**wl.context_kwargs(w, "v"))
+    oenc.get_tables(kc)
+    oenc.get_tables(vc)
+    K, V = wl.kv_pair(w, "cpu")
+    Q = wl.queries(w, "cpu")   # [B, Hq, Tq, d]
+    Ts = 256
+    while True:
+        k = K[0, 0, :Ts].float().double().numpy()
+        v = V[0, 0, :Ts].float().double().numpy()
+        q = Q[0, :G, :Ts].double().numpy()
+        t0 = time.perf_counter()
+        kp = oenc.encode(k, kc)
+        vp = oenc.encode(v, vc)
+        t1 = time.perf_counter()
+        kpl = {x: kp[x][None, None] for x in ("codes", "norms", "signs", "rnorms") if x in kp}
+        vpl = {x: vp[x][None, None] for x in ("codes", "norms")}
+        odec.attend_prefill(q[None], kpl, vpl, kc, vc, [Ts])
+        t2 = time.perf_counter()
+        if t2 - t0 > budget_s / 4 or Ts * 2 > w.extra["Tq"]:
+            break
+        Ts *= 2
+    enc_s, pf_s = t1 - t0, t2 - t1
+    bpt = packed_bytes_per_token_head(w, kc.code_bytes, vc.code_bytes, kc.sign_bytes)
+    pairs = Ts * (Ts + 1) // 2
+    return {"value": round(Ts * bpt / pf_s / 1e9, 6), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"batch 0, KV head 0 ({G} query heads), a {Ts}-position prompt; encode {enc_s:.2f} s, "
+                      f"causal prefill {pf_s:.2f} s; float64 numpy",
+            "tflop_s": round(G * pairs * 4 * w.d / pf_s / 1e12, 8),
+            "host_cpus": os.cpu_count(), "blas_threads": int(blas)}
+
+
 def bench_search(args, w):
     """Search workload: encode the database (turbo4 + QJL, d = 256), then the
     fused top-k scorer for all queries.  value = packed database bytes
@@ -330,6 +375,8 @@ def bench_prefill(args, w):
                             "traffic": traffic_from_profiles("encode", w.name), "algorithmic_bytes": int(enc_bytes / 2),
                             "avg_ms": round(enc_ms / 2, 5)},
     }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_prefill(w)
     print(json.dumps(line), flush=True)
 
 
