@@ -63,6 +63,10 @@ constexpr int kWaveLds = kStage + kPTile;
 static_assert(kG * (kD + 2) * 4 <= kWaveLds, "wave results fit the wave's LDS");
 constexpr float kSlack = 10.0f;  // w <= e^10 ~ 2.2e4 stays well inside fp16
 constexpr int kRsrcWord3 = 0x00020000;
+// Cache policy of the packed-cache loads: non-temporal (each byte is read
+// once per call).  A loads-only copy of the kernel's access pattern streams
+// the 128K layer's 419 MB in 63 us with it against 71 us without.
+constexpr int kNT = 2;
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
@@ -140,23 +144,23 @@ __device__ __forceinline__ void buf_dwords(__amdgpu_buffer_rsrc_t r, uint32_t vo
     int k = 0;
 #pragma unroll
     for (; k + 4 <= N; k += 4) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 4 * k, soff, 0);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 4 * k, soff, kNT);
         w[k] = v.x;
         w[k + 1] = v.y;
         w[k + 2] = v.z;
         w[k + 3] = v.w;
     }
     if constexpr (N % 4 == 3) {
-        const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, voff + 4 * (N - 3), soff, 0);
+        const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, voff + 4 * (N - 3), soff, kNT);
         w[N - 3] = v.x;
         w[N - 2] = v.y;
         w[N - 1] = v.z;
     } else if constexpr (N % 4 == 2) {
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff + 4 * (N - 2), soff, 0);
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff + 4 * (N - 2), soff, kNT);
         w[N - 2] = v.x;
         w[N - 1] = v.y;
     } else if constexpr (N % 4 == 1) {
-        w[N - 1] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 4 * (N - 1), soff, 0);
+        w[N - 1] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 4 * (N - 1), soff, kNT);
     }
 }
 
@@ -282,18 +286,18 @@ void attend_mfma_kernel(const dev_tables kt, const dev_tables vt,
         if constexpr (BN) {
             const __amdgpu_buffer_rsrc_t rkn = make_rsrc(kn0 + kj * 4, left * ks2 * 8);
 #pragma unroll
-            for (int tg = 0; tg < 4; ++tg) r.nkb[tg] = __builtin_amdgcn_raw_buffer_load_b16(rkn, vo_knb[tg], 0, 0);
+            for (int tg = 0; tg < 4; ++tg) r.nkb[tg] = __builtin_amdgcn_raw_buffer_load_b16(rkn, vo_knb[tg], 0, kNT);
             const __amdgpu_buffer_rsrc_t rvn = make_rsrc(vn0 + vj * 4, left * vs2 * 8);
 #pragma unroll
-            for (int hp = 0; hp < kPasses; ++hp) r.nvb[hp] = __builtin_amdgcn_raw_buffer_load_b64(rvn, vo_vnb[hp], 0, 0);
-            r.nvb[kPasses] = __builtin_amdgcn_raw_buffer_load_b64(rvn, vo_vn * 4, 0, 0);
+            for (int hp = 0; hp < kPasses; ++hp) r.nvb[hp] = __builtin_amdgcn_raw_buffer_load_b64(rvn, vo_vnb[hp], 0, kNT);
+            r.nvb[kPasses] = __builtin_amdgcn_raw_buffer_load_b64(rvn, vo_vn * 4, 0, kNT);
         } else {
-            r.nk = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(kn0 + kj, left * ks2 * 2), vo_kn, 0, 0);
-            r.nv = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(vn0 + vj, left * vs2 * 2), vo_vn, 0, 0);
+            r.nk = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(kn0 + kj, left * ks2 * 2), vo_kn, 0, kNT);
+            r.nv = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(vn0 + vj, left * vs2 * 2), vo_vn, 0, kNT);
         }
         if constexpr (QJL) {
             buf_dwords<4>(make_rsrc(ks0 + kj * (kD / 8), left * ks2 * (kD / 8)), vo_ks, 0, r.ks);
-            r.kr = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(kr0 + kj, left * ks2 * 2), vo_kn, 0, 0);
+            r.kr = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(kr0 + kj, left * ks2 * 2), vo_kn, 0, kNT);
         }
     };
 
